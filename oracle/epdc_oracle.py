@@ -1,0 +1,350 @@
+"""CPU oracle for MoE token dispatch and combine.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or run anything in this directory.  The HIP library never calls it and
+shares no code, table or constant generator with it.
+
+Every function is the plain definition of one step, written with numpy in the
+order the pages state it, with no blocking or fusion.  Hidden rows are handled
+as raw bf16 bit patterns (``uint16``) so that copies are compared bit for bit.
+
+Sources (page title, then the section the step follows):
+
+* [axolotl] "integrations.expert_parallel.torch_dispatch" (axolotl API docs):
+  module overview (DeepEP-compatible send layout, K-wide local ids and
+  weights), ``compute_send_counts``, ``build_send_layout``, ``dispatch``,
+  ``combine``, ``chunk_bounds``, ``dispatch_chunked_forward``.
+* [uccl] "nemo_automodel.components.moe.uccl_ep.buffer" (NeMo AutoModel API
+  docs): ``Buffer.get_dispatch_layout``, ``Buffer.dispatch`` (fp8 tuple with
+  one float scale per 128 channels), ``Buffer.combine``,
+  ``Buffer.low_latency_dispatch``.
+* [vllm] "vllm.model_executor.layers.fused_moe.prepare_finalize" (vLLM API
+  docs): ``BatchedPrepareAndFinalize.prepare`` / ``finalize``.
+* [nemo] "nemo_automodel.components.moe.megatron.token_dispatcher" (NeMo
+  AutoModel API docs): ``TokenDispatcherConfig.moe_router_dtype`` (fp32 for
+  routing and for the weighted average of expert outputs).
+
+Readings taken where the pages are silent (each is listed in the design
+notes): combine is weighted per slot and accumulates in float32, product
+rounded then sum rounded, k ascending, starting from +0.0, rounded once to
+bf16 (nearest, ties to even); fp8 is OCP E4M3 (``float8_e4m3fn``) with
+``scale = amax / 448`` in float32, the quotient ``x / scale`` rounded to
+float32 and then to the nearest e4m3 value (ties to even), saturating at 448,
+and an all-zero group giving scale 0 and code 0x00.
+
+Parity pins: every function here is checked by ``tests/test_oracle_*.py``
+against brute force, closed forms, library routines (numpy sorts and
+bincounts, torch's bf16 and float8_e4m3fn conversions) and a hand-worked
+example; none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "chunk_bounds",
+    "validate_routing",
+    "compute_send_counts",
+    "build_send_layout",
+    "dispatch_permute",
+    "bf16_to_f32",
+    "f32_to_bf16",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_rows_fp8",
+    "dequantize_rows_fp8",
+    "dispatch_permute_fp8",
+    "batched_prepare",
+    "combine",
+    "FP8_MAX",
+    "FP8_GROUP",
+]
+
+FP8_MAX = 448.0   # largest finite OCP E4M3 magnitude (S.1111.110)
+FP8_GROUP = 128   # channels per fp32 scale ([uccl] Buffer.dispatch)
+
+
+# --------------------------------------------------------------------------
+# Routing metadata
+# --------------------------------------------------------------------------
+
+def chunk_bounds(num_tokens: int, chunks: int):
+    """[axolotl] chunk_bounds: ``chunks`` contiguous [start, end) ranges.
+
+    All chunks but the last hold ``num_tokens // chunks`` tokens; the last one
+    takes the remainder, so leading chunks are empty when num_tokens < chunks.
+    """
+    if chunks < 1:
+        raise ValueError("chunks must be >= 1")
+    size = num_tokens // chunks
+    out = []
+    for i in range(chunks):
+        start = i * size
+        end = num_tokens if i == chunks - 1 else (i + 1) * size
+        out.append((start, end))
+    return out
+
+
+def validate_routing(topk_idx: np.ndarray, num_experts: int) -> None:
+    """Preconditions of the routing input ([axolotl] dispatch; [uccl]
+    Buffer.dispatch): int64 ids in [-1, E) with -1 meaning unrouted, and the
+    routed ids of one token distinct (a router's top-k never repeats)."""
+    idx = np.asarray(topk_idx)
+    if idx.ndim != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    if idx.size and (idx.min() < -1 or idx.max() >= num_experts):
+        raise ValueError("expert id outside [-1, E)")
+    for t in range(idx.shape[0]):
+        routed = idx[t][idx[t] >= 0]
+        if len(np.unique(routed)) != len(routed):
+            raise ValueError(f"token {t} repeats an expert id")
+
+
+def compute_send_counts(topk_idx, num_ranks, num_local_experts, num_chunks=1):
+    """[axolotl] compute_send_counts and [uccl] Buffer.get_dispatch_layout.
+
+    Returns ``dest`` int32 [T,K] (owning destination of each slot, -1 where
+    unrouted), ``is_in_rank`` uint8 [T,P] (token has at least one expert on
+    destination p), ``send_counts`` int32 [C,P] (tokens sent to p from chunk c)
+    and ``tokens_per_expert`` int32 [C,E] (routed slots naming expert e in
+    chunk c).  Destination p owns experts [p*E_local, (p+1)*E_local).
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    P, El = int(num_ranks), int(num_local_experts)
+    E = P * El
+    validate_routing(idx, E)
+
+    dest = np.where(idx >= 0, idx // El, -1).astype(np.int32)
+    is_in_rank = np.zeros((T, P), dtype=np.uint8)
+    for p in range(P):
+        is_in_rank[:, p] = (dest == p).any(axis=1)
+
+    C = int(num_chunks)
+    send_counts = np.zeros((C, P), dtype=np.int32)
+    tokens_per_expert = np.zeros((C, E), dtype=np.int32)
+    for c, (s, e) in enumerate(chunk_bounds(T, C)):
+        send_counts[c] = is_in_rank[s:e].sum(axis=0)
+        for ex in range(E):
+            tokens_per_expert[c, ex] = int((idx[s:e] == ex).sum())
+    return dest, is_in_rank, send_counts, tokens_per_expert
+
+
+def build_send_layout(topk_idx, topk_weights, num_ranks, num_local_experts):
+    """[axolotl] build_send_layout plus the module overview's layout contract.
+
+    Send rows are ordered destination-major, then token-ascending: for p in
+    0..P-1 and, inside p, for every token t with is_in_rank[t,p] in ascending
+    order, the next row n is taken.  Row n carries
+    ``send_token_idx[n] = t``, ``send_rank[n] = p``,
+    ``send_idx[n,k] = id - p*E_local`` on slots owned by p and -1 elsewhere,
+    ``send_w[n,k] = w[t,k]`` on those slots and +0.0 elsewhere.
+    ``token_row[t,k]`` is the send row of slot k's owner (-1 if unrouted); it
+    is the inverse map that combine uses to find the expert output of a slot.
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_weights, dtype=np.float32)
+    T, K = idx.shape
+    P, El = int(num_ranks), int(num_local_experts)
+    dest, is_in_rank, _, _ = compute_send_counts(idx, P, El, 1)
+
+    N = int(is_in_rank.sum())
+    send_token_idx = np.zeros(N, dtype=np.int32)
+    send_rank = np.zeros(N, dtype=np.int32)
+    send_idx = np.full((N, K), -1, dtype=np.int32)
+    send_w = np.zeros((N, K), dtype=np.float32)
+    token_row = np.full((T, K), -1, dtype=np.int32)
+
+    n = 0
+    for p in range(P):
+        for t in np.flatnonzero(is_in_rank[:, p]):
+            owned = dest[t] == p
+            send_token_idx[n] = t
+            send_rank[n] = p
+            send_idx[n, owned] = idx[t, owned] - p * El
+            send_w[n, owned] = w[t, owned]
+            token_row[t, owned] = n
+            n += 1
+    assert n == N
+    return send_token_idx, send_rank, send_idx, send_w, token_row
+
+
+def dispatch_permute(x_bits, send_token_idx):
+    """[axolotl] dispatch: row n of the send buffer is hidden row
+    send_token_idx[n], copied bit for bit (tokens with no routed expert are
+    not sent)."""
+    x = np.asarray(x_bits)
+    return x[np.asarray(send_token_idx, dtype=np.int64)].copy()
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def bf16_to_f32(bits):
+    """bf16 is the upper half of an IEEE binary32 word."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    return (b << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16(values):
+    """Round float32 to bf16, to nearest with ties to even (finite inputs).
+
+    bf16 keeps the upper 16 bits of binary32.  The two candidates are the
+    truncated magnitude and the next bf16 magnitude up; the dropped 16 bits
+    decide, and an exact half picks the candidate whose last kept bit is 0.
+    """
+    u = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32)
+    lower = u & np.uint32(0xFFFF0000)
+    upper = lower + np.uint32(0x10000)
+    rem = u & np.uint32(0xFFFF)
+    half = np.uint32(0x8000)
+    lower_even = ((lower >> np.uint32(16)) & np.uint32(1)) == 0
+    pick_upper = (rem > half) | ((rem == half) & ~lower_even)
+    out = np.where(pick_upper, upper, lower)
+    return (out >> np.uint32(16)).astype(np.uint16)
+
+
+def e4m3_decode(codes):
+    """Value of OCP E4M3 (float8_e4m3fn) codes: 1 sign, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); no
+    infinities; S.1111.111 is NaN.  Returned as float64 (exact)."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+# Positive finite e4m3 values in code order 0x00..0x7E (ascending magnitude).
+_E4M3_POS = e4m3_decode(np.arange(0x7F))
+
+
+def e4m3_encode(values):
+    """Nearest OCP E4M3 code of each float32 value, ties to the even code
+    (mantissa LSB 0); magnitudes at or above 448 saturate to 448; the sign
+    bit is kept, so -0.0 and negative values that round to zero give 0x80."""
+    v = np.asarray(values, dtype=np.float32)
+    sign = (v.view(np.uint32) >> np.uint32(31)).astype(np.int64)
+    mag = np.abs(v.astype(np.float64))
+    hi = np.searchsorted(_E4M3_POS, mag, side="left")        # POS[hi] >= mag
+    hi = np.clip(hi, 0, len(_E4M3_POS) - 1)
+    lo = np.clip(hi - 1, 0, len(_E4M3_POS) - 1)
+    d_lo = mag - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - mag
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo)
+    code = np.where(mag >= FP8_MAX, 0x7E, code)
+    code = np.where(mag == 0.0, 0, code)
+    return (code | (sign << 7)).astype(np.uint8)
+
+
+def quantize_rows_fp8(x_bits):
+    """[uccl] Buffer.dispatch / low_latency_dispatch fp8 input: e4m3 rows plus
+    one float32 scale per token per 128 channels.
+
+    For each group of 128 channels: amax = max |x| (exact), scale =
+    fl32(amax / 448), q = e4m3(fl32(x / scale)).  A group whose amax is 0
+    gets scale 0.0 and all codes 0x00.  Returns (uint8 [R,H], float32
+    [R, H/128]).
+    """
+    x = bf16_to_f32(x_bits)
+    R, H = x.shape
+    if H % FP8_GROUP:
+        raise ValueError("H must be a multiple of 128 for fp8")
+    g = x.reshape(R, H // FP8_GROUP, FP8_GROUP)
+    amax = np.abs(g).max(axis=2)
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    quot = (g / safe[:, :, None]).astype(np.float32)
+    q = e4m3_encode(quot)
+    q = np.where((scale > 0)[:, :, None], q, np.uint8(0))
+    return q.reshape(R, H).astype(np.uint8), scale
+
+
+def dequantize_rows_fp8(q, scales):
+    """bf16 bits of fl32(decode(q) * scale) per element: the expert output of
+    an identity expert fed with the fp8 rows (used as the combine input)."""
+    q = np.asarray(q, dtype=np.uint8)
+    R, H = q.shape
+    vals = e4m3_decode(q).astype(np.float32).reshape(R, H // FP8_GROUP, FP8_GROUP)
+    prod = (vals * np.asarray(scales, dtype=np.float32)[:, :, None]).astype(np.float32)
+    return f32_to_bf16(prod.reshape(R, H))
+
+
+def dispatch_permute_fp8(x_bits, send_token_idx):
+    """fp8 quantize-on-dispatch: row n holds the quantized hidden row of token
+    send_token_idx[n] and its scales (quantization is per token, so it does
+    not depend on which destination the row goes to)."""
+    q, s = quantize_rows_fp8(x_bits)
+    rows = np.asarray(send_token_idx, dtype=np.int64)
+    return q[rows].copy(), s[rows].copy()
+
+
+# --------------------------------------------------------------------------
+# Expert-batched layout
+# --------------------------------------------------------------------------
+
+def batched_prepare(x_bits, topk_idx, first_expert, num_local_experts,
+                    max_num_tokens):
+    """[vllm] BatchedPrepareAndFinalize.prepare, unquantized branch.
+
+    The buffer [E_local, max_num_tokens, H] starts zeroed.  For local expert e
+    (global id first+e) the tokens that name it in any slot take slots
+    0, 1, 2, ... in ascending token order (running count minus one), and the
+    token's hidden row is stored there.  tokens_per_expert[e] is that count.
+    token_row[t,k] = e*max_num_tokens + slot for local slots, else -1.
+    """
+    x = np.asarray(x_bits, dtype=np.uint16)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    H = x.shape[1]
+    El, M = int(num_local_experts), int(max_num_tokens)
+    b_x = np.zeros((El, M, H), dtype=np.uint16)
+    tokens_per_expert = np.zeros(El, dtype=np.int32)
+    token_row = np.full((T, K), -1, dtype=np.int32)
+    for e in range(El):
+        hit_slots = idx == (first_expert + e)
+        tokens = np.flatnonzero(hit_slots.any(axis=1))
+        if len(tokens) > M:
+            raise ValueError(f"expert {first_expert + e} receives {len(tokens)}"
+                             f" tokens > max_num_tokens={M}")
+        tokens_per_expert[e] = len(tokens)
+        for slot, t in enumerate(tokens):
+            b_x[e, slot] = x[t]
+            token_row[t, hit_slots[t]] = e * M + slot
+    return b_x, tokens_per_expert, token_row
+
+
+# --------------------------------------------------------------------------
+# Combine
+# --------------------------------------------------------------------------
+
+def combine(y_bits, token_row, topk_weights):
+    """[axolotl] combine, [uccl] Buffer.combine / low_latency_combine,
+    [vllm] BatchedPrepareAndFinalize.finalize: the weighted per-token sum of
+    expert outputs back onto the source tokens.
+
+    out[t] = bf16( sum over k = 0..K-1 with r = token_row[t,k] >= 0 of
+    w[t,k] * y[r] ), accumulated in float32 ([nemo] moe_router_dtype): each
+    product is rounded to float32, then added to the running float32 sum
+    (which starts at +0.0) in ascending k.  Tokens with no routed slot give 0.
+    """
+    y = np.asarray(y_bits, dtype=np.uint16)
+    row = np.asarray(token_row, dtype=np.int64)
+    w = np.asarray(topk_weights, dtype=np.float32)
+    T, K = row.shape
+    H = y.shape[1]
+    acc = np.zeros((T, H), dtype=np.float32)
+    for k in range(K):
+        r = row[:, k]
+        m = r >= 0
+        if not m.any():
+            continue
+        prod = (w[m, k][:, None] * bf16_to_f32(y[r[m]])).astype(np.float32)
+        acc[m] = (acc[m] + prod).astype(np.float32)
+    return f32_to_bf16(acc)

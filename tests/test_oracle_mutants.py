@@ -1,0 +1,154 @@
+"""Planted-mistake check for the oracle's pins.
+
+Each case copies the oracle's source, plants one plausible mistake (a dropped
+term, a wrong index, a reversed order, a wrong rounding rule) and runs a few
+pins against the copy on the CPU.  At least one pin must fail, which shows the
+pins constrain that part of the oracle.  The real oracle is never modified.
+"""
+
+import json
+import os
+import types
+
+import numpy as np
+import pytest
+
+import tests.test_oracle_numerics as NUM
+import tests.test_oracle_routing as RT
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC_PATH = os.path.join(os.path.dirname(HERE), "oracle", "epdc_oracle.py")
+with open(SRC_PATH) as f:
+    SRC = f.read()
+with open(os.path.join(HERE, "golden", "hand_worked_tiny.json")) as f:
+    GOLDEN = json.load(f)
+
+
+def make_mutant(old, new):
+    """Copy of the oracle with ``old`` replaced by ``new`` (str or lists)."""
+    olds = [old] if isinstance(old, str) else old
+    news = [new] if isinstance(new, str) else new
+    src = SRC
+    for o, n in zip(olds, news):
+        assert src.count(o) >= 1, f"mutation anchor not found: {o!r}"
+        src = src.replace(o, n, 1)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def pin(module, name, *args):
+    return (module, name, args)
+
+
+ROUTING_PINS = [
+    pin(RT, "test_hand_worked_metadata", GOLDEN),
+    pin(RT, "test_layout_equals_lexsort", "tiny"),
+    pin(RT, "test_layout_invariants_skewed"),
+    pin(RT, "test_chunk_bounds_cases", GOLDEN),
+]
+COMBINE_PINS = [
+    pin(NUM, "test_combine_hand_worked", GOLDEN),
+    pin(NUM, "test_combine_order_is_k_ascending"),
+    pin(NUM, "test_combine_rounds_product_before_sum"),
+    pin(NUM, "test_combine_identity_round_trip_within_1ulp"),
+    pin(NUM, "test_combine_k1_weight1_is_copy_and_unrouted_is_zero"),
+]
+FORMAT_PINS = [
+    pin(NUM, "test_bf16_rne_matches_torch"),
+    pin(NUM, "test_e4m3_encode_matches_torch"),
+    pin(NUM, "test_e4m3_hand_cases", GOLDEN),
+    pin(NUM, "test_quantize_hand_row", GOLDEN),
+    pin(NUM, "test_quantize_properties"),
+]
+BATCHED_PINS = [
+    pin(RT, "test_batched_equals_stable_argsort", 0, 32),
+    pin(RT, "test_hand_worked_permute_and_batched", GOLDEN),
+]
+
+MUTANTS = {
+    "chunk_last_no_remainder": (
+        "end = num_tokens if i == chunks - 1 else (i + 1) * size",
+        "end = (i + 1) * size", ROUTING_PINS),
+    "owner_strided_not_contiguous": (
+        "dest = np.where(idx >= 0, idx // El, -1).astype(np.int32)",
+        "dest = np.where(idx >= 0, idx % P, -1).astype(np.int32)", ROUTING_PINS),
+    "tokens_descending_in_segment": (
+        "for t in np.flatnonzero(is_in_rank[:, p]):",
+        "for t in np.flatnonzero(is_in_rank[:, p])[::-1]:", ROUTING_PINS),
+    "local_id_not_rebased": (
+        "send_idx[n, owned] = idx[t, owned] - p * El",
+        "send_idx[n, owned] = idx[t, owned]", ROUTING_PINS),
+    "weights_copied_on_all_slots": (
+        "send_w[n, owned] = w[t, owned]",
+        "send_w[n] = w[t]", ROUTING_PINS),
+    "counts_per_slot_not_per_token": (
+        "is_in_rank[:, p] = (dest == p).any(axis=1)",
+        "is_in_rank[:, p] = np.minimum((dest == p).sum(axis=1), 1) * 0 + (dest == p).sum(axis=1)",
+        ROUTING_PINS),
+    "combine_k_descending": (
+        "for k in range(K):\n        r = row[:, k]",
+        "for k in reversed(range(K)):\n        r = row[:, k]", COMBINE_PINS),
+    "combine_unweighted": (
+        "prod = (w[m, k][:, None] * bf16_to_f32(y[r[m]])).astype(np.float32)",
+        "prod = bf16_to_f32(y[r[m]]).astype(np.float32)", COMBINE_PINS),
+    "combine_f64_accumulate": (
+        ["acc = np.zeros((T, H), dtype=np.float32)",
+         "acc[m] = (acc[m] + prod).astype(np.float32)"],
+        ["acc = np.zeros((T, H), dtype=np.float64)",
+         "acc[m] = acc[m] + prod"], COMBINE_PINS),
+    "combine_fused_multiply_add": (
+        ["prod = (w[m, k][:, None] * bf16_to_f32(y[r[m]])).astype(np.float32)",
+         "acc[m] = (acc[m] + prod).astype(np.float32)"],
+        ["prod = w[m, k][:, None].astype(np.float64) * bf16_to_f32(y[r[m]])",
+         "acc[m] = (acc[m] + prod).astype(np.float32)"], COMBINE_PINS),
+    "combine_truncating_bf16": (
+        "pick_upper = (rem > half) | ((rem == half) & ~lower_even)",
+        "pick_upper = rem < 0", COMBINE_PINS + FORMAT_PINS[:1]),
+    "bf16_ties_away": (
+        "pick_upper = (rem > half) | ((rem == half) & ~lower_even)",
+        "pick_upper = rem >= half", FORMAT_PINS),
+    "e4m3_ties_away": (
+        "take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))",
+        "take_hi = d_hi <= d_lo", FORMAT_PINS),
+    "e4m3_bias_8": (
+        "(1.0 + m / 8.0) * 2.0 ** (e - 7.0)",
+        "(1.0 + m / 8.0) * 2.0 ** (e - 8.0)", FORMAT_PINS),
+    "fp8_scale_from_max_not_448": (
+        "scale = (amax / np.float32(FP8_MAX)).astype(np.float32)",
+        "scale = (amax / np.float32(240.0)).astype(np.float32)", FORMAT_PINS),
+    "fp8_group_64": ("FP8_GROUP = 128", "FP8_GROUP = 64", FORMAT_PINS),
+    "fp8_zero_group_sign": (
+        "q = np.where((scale > 0)[:, :, None], q, np.uint8(0))",
+        "q = np.where((scale > 0)[:, :, None], q, np.uint8(0x80))", FORMAT_PINS),
+    "batched_slots_descending": (
+        "tokens = np.flatnonzero(hit_slots.any(axis=1))",
+        "tokens = np.flatnonzero(hit_slots.any(axis=1))[::-1]", BATCHED_PINS),
+    "batched_row_stride_wrong": (
+        "token_row[t, hit_slots[t]] = e * M + slot",
+        "token_row[t, hit_slots[t]] = e * (M - 1) + slot", BATCHED_PINS),
+    "batched_padding_not_zero": (
+        "b_x = np.zeros((El, M, H), dtype=np.uint16)",
+        "b_x = np.ones((El, M, H), dtype=np.uint16)", BATCHED_PINS),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    old, new, pins = MUTANTS[name]
+    mod = make_mutant(old, new)
+    failures = []
+    for module, fn, args in pins:
+        monkeypatch.setattr(module, "O", mod)
+        try:
+            getattr(module, fn)(*args)
+        except (AssertionError, ValueError, IndexError) as e:   # the pin fired
+            failures.append((fn, type(e).__name__))
+    assert failures, f"no pin caught mutant {name}"
+
+
+def test_unmutated_copy_passes_all_pins(monkeypatch):
+    mod = make_mutant("FP8_GROUP = 128", "FP8_GROUP = 128")
+    for module, fn, args in ROUTING_PINS + COMBINE_PINS + FORMAT_PINS + BATCHED_PINS:
+        monkeypatch.setattr(module, "O", mod)
+        getattr(module, fn)(*args)
