@@ -1,0 +1,442 @@
+#!/usr/bin/env python3
+"""Throughput of MoE token dispatch + combine on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of seeded synthetic
+routing, with inputs already resident in HBM:
+  send layouts:  counts -> send layout -> row permute -> combine
+  batched:       batched prepare (zero-padded) -> combine
+  fp8 chunked:   counts (all chunks) -> per chunk, alternating 2 streams:
+                 send layout -> fp8 quantize-permute -> combine
+The identity expert sits between dispatch and combine: combine reads the send
+rows themselves (bf16), or the dequantized fp8 rows prepared before timing.
+
+Prints ONE JSON line.  ``value`` is algorithmic HBM bytes per step / step
+time (GB/s); tokens/s and the fraction of the 8 TB/s HBM peak ride along.
+``roofline`` describes the dominant kernel, timed with HIP events on its own
+stream; ``cpu_baseline`` times the CPU oracle on a bounded token sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s (% of peak) + tokens/s, T=16384 H=7168 E=256 K=8"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "skewed_t16384"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (the minimum each kernel must move)
+# ---------------------------------------------------------------------------
+
+def bytes_counts(T, K, P, E, C):
+    return 8 * T * K + 4 * T * K + T * P + 4 * C * (P + E)
+
+
+def bytes_layout(T, K, P, N):
+    return (8 + 4 + 4) * T * K + 4 * P + N * (8 + 8 * K) + 4 * T * K
+
+
+def bytes_permute(H, U, N):
+    return 2 * H * U + 2 * H * N
+
+
+def bytes_permute_fp8(H, U, N):
+    return 2 * H * U + N * (H + 4 * (H // 128))
+
+
+def bytes_combine(H, T, K, R):
+    return 2 * H * R + 8 * T * K + 2 * H * T
+
+
+def bytes_batched(H, T, K, El, M, U_local):
+    return 2 * H * U_local + 8 * T * K + 2 * H * El * M + 4 * El + 4 * T * K
+
+
+# ---------------------------------------------------------------------------
+
+class Timer:
+    """HIP events around each kernel launch, on the launching stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def start(self, name, stream):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        return (name, ev, stream)
+
+    def stop(self, tok):
+        name, ev0, stream = tok
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev1.record(stream)
+        self.pairs.setdefault(name, []).append((ev0, ev1))
+
+    def averages_us(self):
+        return {k: 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in v]))
+                for k, v in self.pairs.items()}
+
+
+def build_send_step(torch, ep, s, d_idx, d_w, d_x):
+    T, K, P, El, H = s.T, s.K, s.P, s.E_local, s.H
+    cap = T * min(K, P)
+    dev = d_x.device
+    counts = ep.ep_compute_send_counts(d_idx, P, El, 1)
+    lay = ep.ep_build_send_layout(d_idx, d_w, counts.dest, counts.send_counts[0], P, El, cap)
+    send_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = ep.workspace_for(ep.ep_layout_workspace_bytes(T, P), dev)
+
+    def step(timer=None):
+        st = torch.cuda.current_stream()
+        tk = timer.start("counts", st) if timer else None
+        ep.ep_compute_send_counts(d_idx, P, El, 1, out=counts)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("layout", st)
+        ep.ep_build_send_layout(d_idx, d_w, counts.dest, counts.send_counts[0], P, El, cap,
+                                out=lay, workspace=ws)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("permute", st)
+        ep.ep_dispatch_permute(d_x, lay.token_row, cap, out=send_x)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("combine", st)
+        ep.ep_combine(send_x, lay.token_row, d_w, out=out)
+        if timer:
+            timer.stop(tk)
+
+    step()
+    torch.cuda.synchronize()
+    N = int(counts.send_counts.sum().item())
+    U = int(((d_idx >= 0).any(dim=1)).sum().item())
+    kb = {
+        "counts": bytes_counts(T, K, P, s.E, 1),
+        "layout": bytes_layout(T, K, P, N),
+        "permute": bytes_permute(H, U, N),
+        "combine": bytes_combine(H, T, K, N),
+    }
+    info = {"num_send": N, "routed_tokens": U, "capacity": cap}
+    return step, kb, info
+
+
+def build_batched_step(torch, ep, s, d_idx, d_w, d_x):
+    T, K, El, H, M = s.T, s.K, s.E_local, s.H, s.max_num_tokens
+    first = s.first_expert
+    dev = d_x.device
+    b_x = torch.empty((El, M, H), dtype=torch.bfloat16, device=dev)
+    tpe = torch.empty(El, dtype=torch.int32, device=dev)
+    trow = torch.empty((T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = ep.workspace_for(ep.ep_batched_workspace_bytes(T, El, M), dev)
+
+    def step(timer=None):
+        st = torch.cuda.current_stream()
+        tk = timer.start("batched_prepare", st) if timer else None
+        ep.ep_batched_prepare(d_x, d_idx, first, El, M, out=b_x, tokens_per_expert=tpe,
+                              token_row=trow, workspace=ws)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("combine", st)
+        ep.ep_combine(b_x, trow, d_w, out=out)
+        if timer:
+            timer.stop(tk)
+
+    step()
+    torch.cuda.synchronize()
+    local = (d_idx >= first) & (d_idx < first + El)
+    U_local = int(local.any(dim=1).sum().item())
+    rows = int(tpe.sum().item())
+    kb = {
+        "batched_prepare": bytes_batched(H, T, K, El, M, U_local),
+        "combine": bytes_combine(H, T, K, rows),
+    }
+    return step, kb, {"rows": rows, "local_tokens": U_local}
+
+
+def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
+    T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, s.chunks
+    dev = d_x.device
+    bounds = ep.chunk_bounds(T, C)
+    streams = [torch.cuda.Stream(device=dev) for _ in range(s.streams)]
+    counts = ep.ep_compute_send_counts(d_idx, P, El, C, expert_counts=False)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    per = []
+    for i, (a, b) in enumerate(bounds):
+        st = streams[i % len(streams)]
+        cap = (b - a) * min(K, P)
+        ws = ep.workspace_for(ep.ep_layout_workspace_bytes(b - a, P), dev, st)
+        with torch.cuda.stream(st):
+            lay = ep.ep_build_send_layout(d_idx[a:b], d_w[a:b], counts.dest[a:b],
+                                          counts.send_counts[i], P, El, cap, stream=st,
+                                          workspace=ws)
+            q, sc = ep.ep_dispatch_permute(d_x[a:b], lay.token_row, cap, fp8=True, stream=st)
+        per.append(dict(a=a, b=b, st=st, cap=cap, lay=lay, q=q, sc=sc, ws=ws))
+    torch.cuda.synchronize()
+    # identity expert behind fp8: y = bf16(decode(q) * scale), built once
+    for c in per:
+        deq = c["q"].float().view(c["cap"], H // 128, 128) * c["sc"][:, :, None]
+        c["y"] = deq.view(c["cap"], H).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+
+    def step(timer=None):
+        start = torch.cuda.Event()
+        start.record(main)
+        tk = timer.start("counts", main) if timer else None
+        ep.ep_compute_send_counts(d_idx, P, El, C, expert_counts=False, out=counts)
+        if timer:
+            timer.stop(tk)
+        ready = torch.cuda.Event()
+        ready.record(main)
+        for i, c in enumerate(per):
+            st = c["st"]
+            st.wait_event(ready)
+            a, b = c["a"], c["b"]
+            tk = timer.start("layout", st) if timer else None
+            ep.ep_build_send_layout(d_idx[a:b], d_w[a:b], counts.dest[a:b],
+                                    counts.send_counts[i], P, El, c["cap"], out=c["lay"],
+                                    workspace=c["ws"], stream=st)
+            if timer:
+                timer.stop(tk)
+                tk = timer.start("permute_fp8", st)
+            ep.ep_dispatch_permute(d_x[a:b], c["lay"].token_row, c["cap"], fp8=True, out=c["q"],
+                                   out_scale=c["sc"], stream=st)
+            if timer:
+                timer.stop(tk)
+                tk = timer.start("combine", st)
+            ep.ep_combine(c["y"], c["lay"].token_row, d_w[a:b], out=out[a:b], stream=st)
+            if timer:
+                timer.stop(tk)
+        for st in streams:
+            done = torch.cuda.Event()
+            done.record(st)
+            main.wait_event(done)
+
+    step()
+    torch.cuda.synchronize()
+    sc_host = counts.send_counts.cpu().numpy()
+    kb = {"counts": bytes_counts(T, K, P, s.E, C), "layout": 0, "permute_fp8": 0, "combine": 0}
+    Ns = []
+    for i, (a, b) in enumerate(bounds):
+        N = int(sc_host[i].sum())
+        U = int(((d_idx[a:b] >= 0).any(dim=1)).sum().item())
+        Ns.append(N)
+        kb["layout"] += bytes_layout(b - a, K, P, N)
+        kb["permute_fp8"] += bytes_permute_fp8(H, U, N)
+        kb["combine"] += bytes_combine(H, b - a, K, N)
+    # per-launch bytes of the chunked kernels: averages over the C launches
+    per_launch = {k: (v / C if k != "counts" else v) for k, v in kb.items()}
+    return step, kb, {"num_send_per_chunk": Ns, "per_launch_bytes": per_launch}
+
+
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(s, budget_tokens):
+    """Time the CPU oracle (single-threaded numpy) on the first
+    ``budget_tokens`` tokens of the same workload, over the same phases."""
+    import oracle as O
+    from epgen import make_hidden, make_routing
+
+    sub = s.replace(T=budget_tokens)
+    idx, w = make_routing(sub)
+    x = make_hidden(sub)
+    T, K, H = sub.T, sub.K, sub.H
+    t0 = time.perf_counter()
+    if s.layout == "batched":
+        bx, tpe, trow = O.batched_prepare(x, idx, s.first_expert, s.E_local, s.max_num_tokens)
+        O.combine(bx.reshape(-1, H), trow, w)
+        U_local = int(((idx >= s.first_expert) & (idx < s.first_expert + s.E_local))
+                      .any(axis=1).sum())
+        nbytes = bytes_batched(H, T, K, s.E_local, s.max_num_tokens, U_local) + \
+            bytes_combine(H, T, K, int(tpe.sum()))
+    else:
+        nbytes = 0
+        for a, b in O.chunk_bounds(T, s.chunks):
+            O.compute_send_counts(idx[a:b], s.P, s.E_local, 1)
+            sti, srk, sidx, sw, trow = O.build_send_layout(idx[a:b], w[a:b], s.P, s.E_local)
+            N = len(sti)
+            U = int((idx[a:b] >= 0).any(axis=1).sum())
+            if s.fp8:
+                q, sc = O.dispatch_permute_fp8(x[a:b], sti)
+                y = O.dequantize_rows_fp8(q, sc)
+                nbytes += bytes_permute_fp8(H, U, N)
+            else:
+                y = O.dispatch_permute(x[a:b], sti)
+                nbytes += bytes_permute(H, U, N)
+            O.combine(y, trow, w[a:b])
+            nbytes += bytes_layout(b - a, K, s.P, N) + bytes_combine(H, b - a, K, N)
+        nbytes += bytes_counts(T, K, s.P, s.E, s.chunks)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(T / dt, 1),
+        "seconds": round(dt, 3),
+        "cores": 1,
+        "host_cpus": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"first {T} tokens of the {s.name} workload (same generator and seed), "
+                  f"all phases, numpy single-threaded",
+    }
+
+
+def traffic_from_profiles(kernel_name, source_digest, launches_per_step):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE,
+    if a committed summary exists for the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens in the CPU-oracle sample (default: sized for ~15 s)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU exchange in this build)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import combine_ep_send_amd as ep
+    from epgen import make_hidden, make_routing, spec
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    ep.lib()                                   # fail loudly if the library is missing
+    s = spec(args.workload)
+    log(f"[bench] workload {s.name}: T={s.T} H={s.H} E={s.E} K={s.K} P={s.P} "
+        f"layout={s.layout} fp8={s.fp8} chunks={s.chunks}")
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    dev = torch.device("cuda:0")
+    d_idx = torch.from_numpy(idx).to(dev)
+    d_w = torch.from_numpy(w).to(dev)
+    d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    del x
+
+    if s.layout == "batched":
+        step, kbytes, info = build_batched_step(torch, ep, s, d_idx, d_w, d_x)
+    elif s.fp8:
+        step, kbytes, info = build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x)
+    else:
+        step, kbytes, info = build_send_step(torch, ep, s, d_idx, d_w, d_x)
+    total_bytes = int(sum(kbytes.values()))
+    log(f"[bench] setup done: {info}; algorithmic bytes/step = {total_bytes / 1e9:.4f} GB")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    # Timed region: K whole steps, per-kernel events inside.
+    timer = Timer(torch)
+    main_stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(main_stream)
+    for _ in range(args.steps):
+        step(timer)
+    ev1.record(main_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms:.4f} ms/step (events), "
+        f"{1000 * wall / args.steps:.4f} ms/step (wall)")
+
+    kern_us = timer.averages_us()
+    per_launch = info.get("per_launch_bytes", kbytes)
+    dom = max((k for k in kern_us if k != "counts" and k != "layout"), key=lambda k: kern_us[k])
+    dom_gbs = per_launch[dom] / (kern_us[dom] * 1e-6) / 1e9
+    src = os.path.join(ROOT, "combine_ep_send_amd", "csrc", "rows.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    traffic = traffic_from_profiles(dom, digest, 1)
+
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not s.fp8 else "fp8-e4m3+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": s.name, "T": s.T, "H": s.H, "E": s.E, "K": s.K, "P": s.P,
+            "routing": s.routing + (f"(s={s.zipf_s})" if s.routing == "zipf" else ""),
+            "unrouted_frac": s.unrouted_frac, "layout": s.layout, "chunks": s.chunks,
+            "streams": s.streams, "seed": s.seed, "parallelism": "single GPU",
+            **{k: v for k, v in info.items() if k != "per_launch_bytes"},
+        },
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(s.T / (ms * 1e-3), 1),
+        "alg_bytes_per_step": total_bytes,
+        "wall_ms_per_step": round(1000 * wall / args.steps, 5),
+        "kernel_avg_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(dom_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": int(per_launch[dom]),
+            "avg_launch_us": round(kern_us[dom], 3),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or {"skewed_t16384": 6144, "uniform_t4096": 4096, "tiny": 256,
+                                "batched_t8192": 8192, "fp8_t32768": 3072}.get(s.name, 1024)
+        log(f"[bench] timing the CPU oracle on {n} tokens")
+        result["cpu_baseline"] = cpu_baseline(s, n)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

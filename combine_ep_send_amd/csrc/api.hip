@@ -1,0 +1,241 @@
+// C ABI of libepdc.so: argument validation on the host, then launches.
+// Nothing here allocates, frees or synchronizes.
+#include <stdint.h>
+
+#include "../../include/epdc.h"
+#include "epdc_launch.h"
+
+namespace {
+
+using namespace epdc;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 30;   // scan values are 30-bit
+constexpr int64_t kMaxExperts = 8192;              // LDS expert histogram
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_LAUNCH; }
+
+// A pointer is acceptable when the array it addresses is empty or the
+// pointer is non-null and aligned to `a` bytes.
+bool arr_ok(const void* p, int64_t count, uintptr_t a) {
+  return count == 0 || (p != nullptr && aligned(p, a));
+}
+
+int check_routing(int64_t T, int K, int P, int El) {
+  if (T < 0 || K < 1 || P < 1 || El < 1) return EP_ERR_INVALID_ARG;
+  if (T >= kMaxTokens || K > EPDC_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+  if (int64_t(P) * El > kMaxExperts) return EP_ERR_UNSUPPORTED;
+  if (T * K > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  return EP_OK;
+}
+
+int check_hidden(int H, bool fp8) {
+  if (H <= 0 || (H % 8) != 0) return EP_ERR_INVALID_ARG;
+  if (fp8 && (H % EPDC_FP8_GROUP) != 0) return EP_ERR_INVALID_ARG;
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_abi_version(void) { return EPDC_ABI_VERSION; }
+
+const char* ep_status_string(int status) {
+  switch (status) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or misaligned pointer)";
+    case EP_ERR_UNSUPPORTED: return "argument outside the supported limits";
+    case EP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case EP_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_bins) {
+  if (num_tokens < 0 || num_bins < 1) return 0;
+  return kWsHeaderBytes + scan_status_bytes(num_tokens, num_bins);
+}
+
+size_t ep_batched_workspace_bytes(int64_t num_tokens, int num_local_experts,
+                                  int64_t max_num_tokens) {
+  if (num_tokens < 0 || num_local_experts < 1 || max_num_tokens < 0) return 0;
+  size_t b = kWsHeaderBytes + scan_status_bytes(num_tokens, num_local_experts);
+  b = (b + 255) & ~size_t(255);
+  return b + size_t(num_local_experts) * size_t(max_num_tokens) * 4u;
+}
+
+int ep_compute_send_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                           int num_ranks, int num_local_experts, int num_chunks, int32_t* dest,
+                           uint8_t* is_in_rank, int32_t* send_counts, int32_t* tokens_per_expert,
+                           int32_t* diag, hipStream_t stream) {
+  int st = check_routing(num_tokens, num_topk, num_ranks, num_local_experts);
+  if (st != EP_OK) return st;
+  if (num_ranks > EPDC_MAX_BINS) return EP_ERR_UNSUPPORTED;
+  if (num_chunks < 1) return EP_ERR_INVALID_ARG;
+  const int64_t TK = num_tokens * num_topk;
+  if (!arr_ok(topk_idx, TK, 8) || !arr_ok(dest, TK, 4) ||
+      !arr_ok(is_in_rank, num_tokens * num_ranks, 4) || !arr_ok(send_counts, 1, 4) ||
+      (tokens_per_expert && !aligned(tokens_per_expert, 4)) || (diag && !aligned(diag, 4)))
+    return EP_ERR_INVALID_ARG;
+  CountArgs a{};
+  a.topk_idx = topk_idx;
+  a.T = num_tokens;
+  a.K = num_topk;
+  a.P = num_ranks;
+  a.E_local = num_local_experts;
+  a.E = num_ranks * num_local_experts;
+  a.C = num_chunks;
+  a.chunk = num_tokens / num_chunks;
+  a.dest = dest;
+  a.is_in_rank = is_in_rank;
+  a.send_counts = send_counts;
+  a.tokens_per_expert = tokens_per_expert;
+  a.diag = diag;
+  return launch_status(launch_counts(a, stream));
+}
+
+int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights, const int32_t* dest,
+                         const int32_t* send_counts, int64_t num_tokens, int num_topk,
+                         int num_ranks, int num_local_experts, int64_t num_send_capacity,
+                         int32_t* send_token_idx, int32_t* send_rank, int32_t* send_idx,
+                         float* send_w, int32_t* token_row, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  int st = check_routing(num_tokens, num_topk, num_ranks, num_local_experts);
+  if (st != EP_OK) return st;
+  if (num_ranks > EPDC_MAX_BINS) return EP_ERR_UNSUPPORTED;
+  if (num_send_capacity < 0) return EP_ERR_INVALID_ARG;
+  if (num_send_capacity > INT32_MAX || num_send_capacity * num_topk > INT32_MAX)
+    return EP_ERR_UNSUPPORTED;
+  const int64_t TK = num_tokens * num_topk;
+  const int64_t cap = num_send_capacity;
+  if (!arr_ok(topk_idx, TK, 8) || !arr_ok(topk_weights, TK, 4) || !arr_ok(dest, TK, 4) ||
+      !arr_ok(send_counts, 1, 4) || !arr_ok(token_row, TK, 4) ||
+      !arr_ok(send_token_idx, cap, 4) || !arr_ok(send_rank, cap, 4) ||
+      !arr_ok(send_idx, cap, 4) || !arr_ok(send_w, cap, 4))
+    return EP_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < ep_layout_workspace_bytes(num_tokens, num_ranks))
+    return EP_ERR_WORKSPACE;
+  ScanArgs a{};
+  a.topk_idx = topk_idx;
+  a.T = num_tokens;
+  a.K = num_topk;
+  a.bins = num_ranks;
+  a.ctrl = static_cast<uint32_t*>(workspace);
+  a.status = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
+  a.token_row = token_row;
+  a.topk_weights = topk_weights;
+  a.dest = dest;
+  a.send_counts = send_counts;
+  a.E_local = num_local_experts;
+  a.capacity = num_send_capacity;
+  a.send_token_idx = send_token_idx;
+  a.send_rank = send_rank;
+  a.send_idx = send_idx;
+  a.send_w = send_w;
+  return launch_status(launch_send_layout(a, stream));
+}
+
+int ep_dispatch_permute(const void* x, int64_t num_tokens, int hidden, const int32_t* token_row,
+                        int num_topk, int64_t num_send_capacity, int out_dtype, void* send_x,
+                        float* send_scale, hipStream_t stream) {
+  if (num_tokens < 0 || num_topk < 1 || num_send_capacity < 0) return EP_ERR_INVALID_ARG;
+  if (num_tokens >= kMaxTokens || num_topk > EPDC_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+  if (num_send_capacity > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  const bool fp8 = out_dtype == EP_DTYPE_FP8_E4M3;
+  if (!fp8 && out_dtype != EP_DTYPE_BF16) return EP_ERR_INVALID_ARG;
+  int st = check_hidden(hidden, fp8);
+  if (st != EP_OK) return st;
+  const int64_t cap = num_send_capacity;
+  if (!arr_ok(x, num_tokens, 16) || !arr_ok(token_row, num_tokens, 4) ||
+      !arr_ok(send_x, cap, 16) || (fp8 && !arr_ok(send_scale, cap, 4)))
+    return EP_ERR_INVALID_ARG;
+  RowArgs a{};
+  a.x = x;
+  a.T = num_tokens;
+  a.H = hidden;
+  a.token_row = token_row;
+  a.K = num_topk;
+  a.capacity = num_send_capacity;
+  a.out = send_x;
+  a.out_scale = fp8 ? send_scale : nullptr;
+  return launch_status(fp8 ? launch_permute_fp8(a, stream) : launch_permute_bf16(a, stream));
+}
+
+int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                       int hidden, int first_expert, int num_local_experts,
+                       int64_t max_num_tokens, void* b_x, int32_t* tokens_per_expert,
+                       int32_t* token_row, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (num_tokens < 0 || num_topk < 1 || num_local_experts < 1 || max_num_tokens < 0 ||
+      first_expert < 0)
+    return EP_ERR_INVALID_ARG;
+  if (num_tokens >= kMaxTokens || num_topk > EPDC_MAX_TOPK ||
+      num_local_experts > EPDC_MAX_BINS || num_tokens * num_topk > INT32_MAX)
+    return EP_ERR_UNSUPPORTED;
+  if (int64_t(num_local_experts) * max_num_tokens > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  int st = check_hidden(hidden, false);
+  if (st != EP_OK) return st;
+  if (!arr_ok(x, num_tokens, 16) || !arr_ok(topk_idx, num_tokens, 8) ||
+      !arr_ok(token_row, num_tokens, 4) || !arr_ok(b_x, max_num_tokens, 16) ||
+      !arr_ok(tokens_per_expert, 1, 4))
+    return EP_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < ep_batched_workspace_bytes(num_tokens, num_local_experts, max_num_tokens))
+    return EP_ERR_WORKSPACE;
+  size_t map_off = kWsHeaderBytes + scan_status_bytes(num_tokens, num_local_experts);
+  map_off = (map_off + 255) & ~size_t(255);
+  int32_t* slot_token = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + map_off);
+
+  ScanArgs a{};
+  a.topk_idx = topk_idx;
+  a.T = num_tokens;
+  a.K = num_topk;
+  a.bins = num_local_experts;
+  a.ctrl = static_cast<uint32_t*>(workspace);
+  a.status = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
+  a.token_row = token_row;
+  a.first_expert = first_expert;
+  a.max_tokens = max_num_tokens;
+  a.slot_token = slot_token;
+  a.tokens_per_expert = tokens_per_expert;
+  hipError_t e = launch_batched_scan(a, stream);
+  if (e != hipSuccess) return EP_ERR_LAUNCH;
+
+  FillArgs f{};
+  f.x = x;
+  f.T = num_tokens;
+  f.H = hidden;
+  f.slot_token = slot_token;
+  f.tokens_per_expert = tokens_per_expert;
+  f.E_local = num_local_experts;
+  f.max_tokens = max_num_tokens;
+  f.b_x = b_x;
+  return launch_status(launch_batched_fill(f, stream));
+}
+
+int ep_combine(const void* y, int64_t num_rows, const int32_t* token_row,
+               const float* topk_weights, int64_t num_tokens, int num_topk, int hidden, void* out,
+               hipStream_t stream) {
+  if (num_tokens < 0 || num_topk < 1 || num_rows < 0) return EP_ERR_INVALID_ARG;
+  if (num_tokens >= kMaxTokens || num_topk > EPDC_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+  int st = check_hidden(hidden, false);
+  if (st != EP_OK) return st;
+  if (!arr_ok(y, num_rows, 16) || !arr_ok(token_row, num_tokens, 4) ||
+      !arr_ok(topk_weights, num_tokens, 4) || !arr_ok(out, num_tokens, 16))
+    return EP_ERR_INVALID_ARG;
+  CombineArgs a{};
+  a.y = y;
+  a.R = num_rows;
+  a.token_row = token_row;
+  a.w = topk_weights;
+  a.T = num_tokens;
+  a.K = num_topk;
+  a.H = hidden;
+  a.out = out;
+  return launch_status(launch_combine(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device-side helpers shared by the epdc kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epdc {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;               // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kTile = kBlock;             // tokens per scan tile (one per thread)
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Wave index as a value the compiler knows is uniform across the wave.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (uint64_t(1) << lane_id()) - 1;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// ---- agent-scope atomics (visible across all XCDs of the device) ----------
+__device__ __forceinline__ uint64_t ld_acquire(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fetch_or(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- 16-byte streaming loads/stores ----------------------------------------
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) {
+  __builtin_nontemporal_store(v, p);
+}
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------
+// A bf16 value is the upper half of a binary32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round a finite fp32 to bf16, to nearest with ties to even: add just under
+// half an ulp of bf16, plus one if the kept LSB is odd, then truncate.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- OCP e4m3 (float8_e4m3fn) encode ----------------------------------------
+// Nearest code with ties to even, saturating at 448 (0x7E), sign kept.
+// Normal range (|v| >= 2^-6): round the binary32 mantissa from 23 to 3 bits
+// on the raw bits (a carry moves into the exponent) and rebias 127 -> 7.
+// Below 2^-6 the codes are the uniform grid m * 2^-9, m = 0..8, so the code
+// is rint(|v| * 2^9) (the scaling is exact; rint rounds ties to even).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                    // |v| >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {              // |v| < 2^-6
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // exp32:mant3
+    code = r - (120u << 3);                  // exponent bias 127 -> 7
+  }
+  return code | sign;
+}
+
+// ---- packed scan status words ------------------------------------------------
+// [63:32] call epoch, [31:30] flag, [29:0] value.
+constexpr uint32_t kFlagNone = 0, kFlagAggregate = 1, kFlagPrefix = 2;
+__device__ __forceinline__ uint64_t pack_status(uint32_t epoch, uint32_t flag, uint32_t value) {
+  return (uint64_t(epoch) << 32) | (uint64_t(flag) << 30) | uint64_t(value & 0x3FFFFFFFu);
+}
+__device__ __forceinline__ uint32_t status_epoch(uint64_t w) { return uint32_t(w >> 32); }
+__device__ __forceinline__ uint32_t status_flag(uint64_t w) { return uint32_t(w >> 30) & 3u; }
+__device__ __forceinline__ uint32_t status_value(uint64_t w) { return uint32_t(w) & 0x3FFFFFFFu; }
+
+}  // namespace epdc

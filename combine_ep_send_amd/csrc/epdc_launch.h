@@ -1,0 +1,102 @@
+// Internal launchers: each enqueues the kernels of one entry point on a
+// stream, after the C-ABI layer has validated every argument.  They return
+// the hipError_t of the launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace epdc {
+
+// Scan workspace: a 256-byte header of uint32 control words followed by one
+// 64-bit status word per (tile, bin).
+constexpr size_t kWsHeaderBytes = 256;
+enum : int { kCtrlTicket = 0, kCtrlDone = 1, kCtrlEpoch = 2, kCtrlError = 3 };
+constexpr uint32_t kErrLookbackGaveUp = 1u;
+
+inline int64_t num_tiles(int64_t T) { return (T + 255) / 256; }
+inline size_t scan_status_bytes(int64_t T, int bins) {
+  int64_t tiles = num_tiles(T) > 0 ? num_tiles(T) : 1;
+  return size_t(tiles) * size_t(bins) * 8u;
+}
+
+struct CountArgs {
+  const int64_t* topk_idx;
+  int64_t T;
+  int K, P, E_local, E, C;
+  int64_t chunk;                 // T / C
+  int32_t* dest;
+  uint8_t* is_in_rank;
+  int32_t* send_counts;
+  int32_t* tokens_per_expert;    // may be null
+  int32_t* diag;                 // may be null
+};
+hipError_t launch_counts(const CountArgs& a, hipStream_t s);
+
+struct ScanArgs {
+  // common
+  const int64_t* topk_idx;
+  int64_t T;
+  int K;
+  int bins;                      // P (send layout) or E_local (batched)
+  uint32_t* ctrl;                // workspace header
+  uint64_t* status;              // [tiles, bins]
+  int32_t* token_row;
+  // send layout
+  const float* topk_weights;
+  const int32_t* dest;
+  const int32_t* send_counts;
+  int E_local;
+  int64_t capacity;
+  int32_t* send_token_idx;
+  int32_t* send_rank;
+  int32_t* send_idx;
+  float* send_w;
+  // batched layout
+  int64_t first_expert;
+  int64_t max_tokens;
+  int32_t* slot_token;           // [E_local, max_tokens]
+  int32_t* tokens_per_expert;    // [E_local]
+};
+hipError_t launch_send_layout(const ScanArgs& a, hipStream_t s);
+hipError_t launch_batched_scan(const ScanArgs& a, hipStream_t s);
+
+struct RowArgs {
+  const void* x;
+  int64_t T;
+  int H;
+  const int32_t* token_row;
+  int K;
+  int64_t capacity;              // rows of the destination buffer
+  void* out;
+  float* out_scale;              // fp8 scales or null
+};
+hipError_t launch_permute_bf16(const RowArgs& a, hipStream_t s);
+hipError_t launch_permute_fp8(const RowArgs& a, hipStream_t s);
+
+struct FillArgs {
+  const void* x;
+  int64_t T;
+  int H;
+  const int32_t* slot_token;
+  const int32_t* tokens_per_expert;
+  int E_local;
+  int64_t max_tokens;
+  void* b_x;
+};
+hipError_t launch_batched_fill(const FillArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const void* y;
+  int64_t R;
+  const int32_t* token_row;
+  const float* w;
+  int64_t T;
+  int K;
+  int H;
+  void* out;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace epdc

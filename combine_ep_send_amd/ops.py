@@ -1,0 +1,272 @@
+"""Thin PyTorch binding of libepdc.so.
+
+The ``ep_*`` functions mirror the C entry points one for one: they check
+dtypes, shapes and devices, allocate outputs the caller did not pass, and
+call the library on the current (or given) HIP stream.  All arithmetic runs
+in the HIP kernels; PyTorch only supplies device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import NamedTuple, Optional
+
+import torch
+
+from ._lib import EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3, check, lib
+
+__all__ = [
+    "Counts",
+    "SendLayout",
+    "ep_compute_send_counts",
+    "ep_build_send_layout",
+    "ep_dispatch_permute",
+    "ep_batched_prepare",
+    "ep_combine",
+    "ep_layout_workspace_bytes",
+    "ep_batched_workspace_bytes",
+    "workspace_for",
+]
+
+
+class Counts(NamedTuple):
+    dest: torch.Tensor                 # int32 [T, K]
+    is_in_rank: torch.Tensor           # uint8 [T, P]
+    send_counts: torch.Tensor          # int32 [C, P]
+    tokens_per_expert: Optional[torch.Tensor]  # int32 [C, E] or None
+    diag: torch.Tensor                 # int32 [1]: ids outside [-1, E)
+
+
+class SendLayout(NamedTuple):
+    send_token_idx: torch.Tensor       # int32 [cap]
+    send_rank: torch.Tensor            # int32 [cap]
+    send_idx: torch.Tensor             # int32 [cap, K]
+    send_w: torch.Tensor               # float32 [cap, K]
+    token_row: torch.Tensor            # int32 [T, K]
+
+
+def _vp(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _gpu(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    return t
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def ep_layout_workspace_bytes(num_tokens: int, num_bins: int) -> int:
+    return int(lib().ep_layout_workspace_bytes(int(num_tokens), int(num_bins)))
+
+
+def ep_batched_workspace_bytes(num_tokens: int, num_local_experts: int, max_num_tokens: int) -> int:
+    return int(lib().ep_batched_workspace_bytes(int(num_tokens), int(num_local_experts),
+                                                int(max_num_tokens)))
+
+
+_WORKSPACES = {}
+
+
+def workspace_for(nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
+    """A zero-initialised scan workspace of at least ``nbytes``, cached per
+    (device, stream).  The kernels leave it ready for the next call, so one
+    workspace serves every call enqueued on its stream."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           s.cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(s):
+            ws = torch.zeros(max(int(nbytes), 1 << 16), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def ep_compute_send_counts(topk_idx: torch.Tensor, num_ranks: int, num_local_experts: int,
+                           num_chunks: int = 1, *, expert_counts: bool = True,
+                           out: Optional[Counts] = None, stream=None) -> Counts:
+    _gpu(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    P, El, C = int(num_ranks), int(num_local_experts), int(num_chunks)
+    E = P * El
+    dev = topk_idx.device
+    if out is None:
+        out = Counts(
+            dest=torch.empty((T, K), dtype=torch.int32, device=dev),
+            is_in_rank=torch.empty((T, P), dtype=torch.uint8, device=dev),
+            send_counts=torch.empty((C, P), dtype=torch.int32, device=dev),
+            tokens_per_expert=(torch.empty((C, E), dtype=torch.int32, device=dev)
+                               if expert_counts else None),
+            diag=torch.empty(1, dtype=torch.int32, device=dev))
+    _shape(_gpu(out.dest, "dest", torch.int32), "dest", (T, K))
+    _shape(_gpu(out.is_in_rank, "is_in_rank", torch.uint8), "is_in_rank", (T, P))
+    _shape(_gpu(out.send_counts, "send_counts", torch.int32), "send_counts", (C, P))
+    if out.tokens_per_expert is not None:
+        _shape(_gpu(out.tokens_per_expert, "tokens_per_expert", torch.int32),
+               "tokens_per_expert", (C, E))
+    _shape(_gpu(out.diag, "diag", torch.int32), "diag", (1,))
+    st = lib().ep_compute_send_counts(
+        _vp(topk_idx), T, K, P, El, C, _vp(out.dest), _vp(out.is_in_rank), _vp(out.send_counts),
+        _vp(out.tokens_per_expert), _vp(out.diag), _stream(stream))
+    check(st, "ep_compute_send_counts")
+    return out
+
+
+def ep_build_send_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+                         dest: torch.Tensor, send_counts: torch.Tensor, num_ranks: int,
+                         num_local_experts: int, num_send_capacity: int, *,
+                         out: Optional[SendLayout] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> SendLayout:
+    _gpu(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    P, El, cap = int(num_ranks), int(num_local_experts), int(num_send_capacity)
+    _shape(_gpu(topk_weights, "topk_weights", torch.float32), "topk_weights", (T, K))
+    _shape(_gpu(dest, "dest", torch.int32), "dest", (T, K))
+    _gpu(send_counts, "send_counts", torch.int32)
+    if send_counts.numel() != P:
+        raise ValueError("send_counts must hold P counts (one chunk)")
+    dev = topk_idx.device
+    if out is None:
+        out = SendLayout(
+            send_token_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+            send_rank=torch.empty(cap, dtype=torch.int32, device=dev),
+            send_idx=torch.empty((cap, K), dtype=torch.int32, device=dev),
+            send_w=torch.empty((cap, K), dtype=torch.float32, device=dev),
+            token_row=torch.empty((T, K), dtype=torch.int32, device=dev))
+    for name, t, dt in (("send_token_idx", out.send_token_idx, torch.int32),
+                        ("send_rank", out.send_rank, torch.int32),
+                        ("send_idx", out.send_idx, torch.int32),
+                        ("send_w", out.send_w, torch.float32)):
+        _gpu(t, name, dt)
+        if t.shape[0] < cap:
+            raise ValueError(f"{name} holds fewer than {cap} rows")
+    if out.send_idx.dim() != 2 or out.send_idx.shape[1] != K or out.send_w.shape[1:] != (K,):
+        raise ValueError("send_idx / send_w must be [cap, K]")
+    _shape(_gpu(out.token_row, "token_row", torch.int32), "token_row", (T, K))
+    nbytes = ep_layout_workspace_bytes(T, P)
+    if workspace is None:
+        workspace = workspace_for(nbytes, dev, stream)
+    _gpu(workspace, "workspace", torch.uint8)
+    st = lib().ep_build_send_layout(
+        _vp(topk_idx), _vp(topk_weights), _vp(dest), _vp(send_counts), T, K, P, El, cap,
+        _vp(out.send_token_idx), _vp(out.send_rank), _vp(out.send_idx), _vp(out.send_w),
+        _vp(out.token_row), _vp(workspace), workspace.numel(), _stream(stream))
+    check(st, "ep_build_send_layout")
+    return out
+
+
+def ep_dispatch_permute(x: torch.Tensor, token_row: torch.Tensor, num_send_capacity: int, *,
+                        fp8: bool = False, out: Optional[torch.Tensor] = None,
+                        out_scale: Optional[torch.Tensor] = None, stream=None):
+    """bf16: returns send_x [cap, H] bf16.  fp8: returns (send_x [cap, H]
+    float8_e4m3fn, send_scale [cap, H/128] float32)."""
+    _gpu(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    _gpu(token_row, "token_row", torch.int32, 2)
+    if token_row.shape[0] != T:
+        raise ValueError("token_row must be [T, K]")
+    K = token_row.shape[1]
+    cap = int(num_send_capacity)
+    dev = x.device
+    if fp8:
+        if out is None:
+            out = torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev)
+        if out_scale is None:
+            out_scale = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
+        _gpu(out, "send_x", torch.float8_e4m3fn)
+        _gpu(out_scale, "send_scale", torch.float32)
+        if out.shape[0] < cap or out.shape[1:] != (H,) or out_scale.shape[0] < cap \
+                or out_scale.shape[1:] != (H // 128,):
+            raise ValueError("send_x / send_scale too small")
+    else:
+        if out is None:
+            out = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        _gpu(out, "send_x", torch.bfloat16)
+        if out.shape[0] < cap or out.shape[1:] != (H,):
+            raise ValueError("send_x too small")
+    st = lib().ep_dispatch_permute(
+        _vp(x), T, H, _vp(token_row), K, cap, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
+        _vp(out), _vp(out_scale) if fp8 else None, _stream(stream))
+    check(st, "ep_dispatch_permute")
+    return (out, out_scale) if fp8 else out
+
+
+def ep_batched_prepare(x: torch.Tensor, topk_idx: torch.Tensor, first_expert: int,
+                       num_local_experts: int, max_num_tokens: int, *,
+                       out: Optional[torch.Tensor] = None,
+                       tokens_per_expert: Optional[torch.Tensor] = None,
+                       token_row: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (b_x [E_local, max, H] bf16, tokens_per_expert [E_local] int32,
+    token_row [T, K] int32)."""
+    _gpu(x, "x", torch.bfloat16, 2)
+    _gpu(topk_idx, "topk_idx", torch.int64, 2)
+    T, H = x.shape
+    if topk_idx.shape[0] != T:
+        raise ValueError("topk_idx must be [T, K]")
+    K = topk_idx.shape[1]
+    El, M = int(num_local_experts), int(max_num_tokens)
+    dev = x.device
+    if out is None:
+        out = torch.empty((El, M, H), dtype=torch.bfloat16, device=dev)
+    if tokens_per_expert is None:
+        tokens_per_expert = torch.empty(El, dtype=torch.int32, device=dev)
+    if token_row is None:
+        token_row = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _shape(_gpu(out, "b_x", torch.bfloat16), "b_x", (El, M, H))
+    _shape(_gpu(tokens_per_expert, "tokens_per_expert", torch.int32), "tokens_per_expert", (El,))
+    _shape(_gpu(token_row, "token_row", torch.int32), "token_row", (T, K))
+    nbytes = ep_batched_workspace_bytes(T, El, M)
+    if workspace is None:
+        workspace = workspace_for(nbytes, dev, stream)
+    _gpu(workspace, "workspace", torch.uint8)
+    st = lib().ep_batched_prepare(
+        _vp(x), _vp(topk_idx), T, K, H, int(first_expert), El, M, _vp(out),
+        _vp(tokens_per_expert), _vp(token_row), _vp(workspace), workspace.numel(),
+        _stream(stream))
+    check(st, "ep_batched_prepare")
+    return out, tokens_per_expert, token_row
+
+
+def ep_combine(y: torch.Tensor, token_row: torch.Tensor, topk_weights: torch.Tensor, *,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out [T, H] bf16 = weighted fp32 sum over k of y[token_row[t, k]].
+    ``y`` is [R, H] or any contiguous bf16 tensor whose last dim is H (e.g.
+    the batched buffer [E_local, max, H], read as E_local*max rows)."""
+    _gpu(y, "y", torch.bfloat16)
+    if y.dim() < 2:
+        raise ValueError("y must be [rows, H]")
+    H = y.shape[-1]
+    R = y.numel() // H if H else 0
+    _gpu(token_row, "token_row", torch.int32, 2)
+    T, K = token_row.shape
+    _shape(_gpu(topk_weights, "topk_weights", torch.float32), "topk_weights", (T, K))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _shape(_gpu(out, "out", torch.bfloat16), "out", (T, H))
+    st = lib().ep_combine(_vp(y), R, _vp(token_row), _vp(topk_weights), T, K, H, _vp(out),
+                          _stream(stream))
+    check(st, "ep_combine")
+    return out

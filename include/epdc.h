@@ -1,0 +1,249 @@
+/*
+ * epdc.h - MoE token dispatch and combine on one MI355X (gfx950).
+ *
+ * C ABI of libepdc.so.  The library computes, on one GPU's share of the work,
+ * what an expert-parallel dispatcher does before and after its all-to-all:
+ * routing counts, a stable destination-major send layout (or the
+ * expert-batched layout), the permuted hidden rows (bf16, or fp8 e4m3 with
+ * per-128-channel scales) and the weighted per-token combine.  The P
+ * "destinations" are contiguous segments of one device buffer; nothing here
+ * talks to another GPU.
+ *
+ * Sources (page title, then the section the call follows):
+ *  - axolotl API docs, "integrations.expert_parallel.torch_dispatch":
+ *    module overview, compute_send_counts, build_send_layout, dispatch,
+ *    combine, chunk_bounds, dispatch_chunked_forward, to_host.
+ *  - NeMo AutoModel API docs, "nemo_automodel.components.moe.uccl_ep.buffer":
+ *    Buffer.get_dispatch_layout, Buffer.dispatch, Buffer.combine,
+ *    Buffer.low_latency_dispatch (fp8 rows + float scales per 128 channels).
+ *  - vLLM API docs, "vllm.model_executor.layers.fused_moe.prepare_finalize":
+ *    BatchedPrepareAndFinalize.prepare / finalize.
+ *  - NeMo AutoModel API docs,
+ *    "nemo_automodel.components.moe.megatron.token_dispatcher":
+ *    TokenDispatcherConfig.moe_router_dtype (fp32 weighted averaging).
+ *
+ * Conventions shared by every call:
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous arrays.
+ *    The caller owns every buffer; the library allocates nothing, frees
+ *    nothing, keeps no state between calls and never synchronizes.  Each call
+ *    only validates its arguments on the host and enqueues kernels on
+ *    `stream`.
+ *  - Shapes use T = num_tokens, K = num_topk, P = num_ranks,
+ *    E_local = num_local_experts, E = P * E_local, H = hidden.
+ *    Destination p owns the experts [p*E_local, (p+1)*E_local).
+ *  - Expert ids are int64 in [-1, E); -1 means "unrouted".  Routed ids of one
+ *    token are expected to be distinct (a router's top-k).  Ids outside
+ *    [-1, E) are treated as unrouted and counted in `diag`.
+ *  - Every index and count written is int32; membership flags are uint8 0/1.
+ *  - Errors: a negative ep_status_t is returned BEFORE anything is enqueued
+ *    when an argument is invalid (null pointer, bad size, misaligned
+ *    pointer, workspace too small); EP_ERR_LAUNCH if the runtime rejects a
+ *    launch.  Conditions only the device can see (capacity overflow, bad
+ *    ids) never fault: rows past a capacity are not written, their slots get
+ *    token_row = -1, and the true counts are still reported.
+ *  - Alignment: hidden-row buffers (x, send_x, y, out, b_x) 16 bytes;
+ *    topk_idx 8 bytes; all other arrays 4 bytes; workspaces 256 bytes.
+ *    A pointer to an empty array (e.g. every [T,..] array when T = 0) may
+ *    be NULL.
+ *  - Limits: 1 <= K <= 16; T < 2^30; P and E_local <= 1024; E <= 8192;
+ *    H a positive multiple of 8 (of 128 for fp8); every row index fits int32.
+ */
+#ifndef EPDC_H
+#define EPDC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = -1,   /* null pointer, bad size or misalignment */
+    EP_ERR_UNSUPPORTED = -2,   /* outside the documented limits */
+    EP_ERR_WORKSPACE = -3,     /* workspace missing or too small */
+    EP_ERR_LAUNCH = -4         /* the HIP runtime rejected a kernel launch */
+} ep_status_t;
+
+typedef enum {
+    EP_DTYPE_BF16 = 0,         /* rows copied bit for bit */
+    EP_DTYPE_FP8_E4M3 = 1      /* OCP e4m3 (float8_e4m3fn) + fp32 scales */
+} ep_dtype_t;
+
+#define EPDC_ABI_VERSION 1
+#define EPDC_MAX_TOPK 16
+#define EPDC_MAX_BINS 1024
+#define EPDC_FP8_GROUP 128
+
+/* Version of this ABI (EPDC_ABI_VERSION). */
+int ep_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* ep_status_string(int status);
+
+/*
+ * Bytes of workspace ep_build_send_layout needs for T tokens and P
+ * destinations (its scan bins).  The workspace holds the cross-workgroup
+ * scan state: a 256-byte header (uint32 words: [0] tile ticket, [1] finished
+ * tiles, [2] call epoch, [3] error flags: bit 0 = a lookback wait gave up)
+ * followed by one 64-bit status word per (tile of 256 tokens, bin).
+ * It must be zero-filled once before its first use; every call leaves it
+ * ready for the next call.  Calls that may overlap in time (different
+ * streams) must use different workspaces.
+ */
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_bins);
+
+/*
+ * Bytes of workspace ep_batched_prepare needs: the scan state above with
+ * E_local bins plus an int32 map [E_local, max_num_tokens] from batch slot to
+ * source token.  Same zero-once / no-overlap rules.
+ */
+size_t ep_batched_workspace_bytes(int64_t num_tokens, int num_local_experts,
+                                  int64_t max_num_tokens);
+
+/*
+ * Routing decode and histograms.
+ * axolotl "torch_dispatch": compute_send_counts; NeMo "uccl_ep.buffer":
+ * Buffer.get_dispatch_layout (num_tokens_per_rank, num_tokens_per_expert,
+ * is_token_in_rank); axolotl chunk_bounds for the per-chunk split.
+ *
+ *   topk_idx           [T,K] int64 in   global expert ids, -1 = unrouted
+ *   num_chunks         C >= 1           chunk c = [c*(T/C), (c+1)*(T/C)),
+ *                                       the last chunk ends at T
+ *   dest               [T,K] int32 out  owning destination id / E_local, or -1
+ *   is_in_rank         [T,P] uint8 out  1 iff some slot of t is owned by p
+ *   send_counts        [C,P] int32 out  sum of is_in_rank over chunk c
+ *   tokens_per_expert  [C,E] int32 out  routed slots naming e in chunk c
+ *                                       (may be NULL)
+ *   diag               [1]   int32 out  ids outside [-1, E) (may be NULL)
+ * All outputs are fully overwritten (counts are cleared by the call).
+ */
+int ep_compute_send_counts(const int64_t* topk_idx, int64_t num_tokens,
+                           int num_topk, int num_ranks, int num_local_experts,
+                           int num_chunks, int32_t* dest, uint8_t* is_in_rank,
+                           int32_t* send_counts, int32_t* tokens_per_expert,
+                           int32_t* diag, hipStream_t stream);
+
+/*
+ * Stable destination-major send layout.
+ * axolotl "torch_dispatch": build_send_layout and the module overview (each
+ * token is sent once to every destination owning one of its experts, with a
+ * K-wide table of local expert ids, -1 on slots owned elsewhere, and fp32
+ * weights, 0 on those slots).
+ *
+ * Rows are ordered by destination, then by ascending token.  With
+ * seg[p] = send_counts[0] + ... + send_counts[p-1], the pair (t, p) takes row
+ * n = seg[p] + #{t' < t : is_in_rank[t', p]}, and the call writes
+ *   send_token_idx[n] = t, send_rank[n] = p,
+ *   send_idx[n,k] = topk_idx[t,k] - p*E_local where dest[t,k] == p, else -1,
+ *   send_w[n,k]   = topk_weights[t,k]           where dest[t,k] == p, else 0,
+ *   token_row[t,k] = n where dest[t,k] == p (row of slot k's owner), -1 for
+ *   unrouted slots.
+ *
+ *   topk_idx, topk_weights  [T,K] int64 / fp32 in
+ *   dest                    [T,K] int32 in   from ep_compute_send_counts
+ *   send_counts             [P]   int32 in   counts of these T tokens (one
+ *                                            chunk's row of the [C,P] array)
+ *   num_send_capacity       rows available in the four send arrays; the exact
+ *                           N = sum(send_counts) (a host copy of the counts)
+ *                           or a bound such as T*min(K,P) that needs no sync.
+ *                           Rows >= capacity are not written.  Rows in
+ *                           [N, capacity) are left untouched.
+ *   send_token_idx, send_rank [cap] int32 out; send_idx [cap,K] int32 out;
+ *   send_w [cap,K] fp32 out; token_row [T,K] int32 out
+ *   workspace               ep_layout_workspace_bytes(T, P) bytes (see there)
+ * The membership flags (is_in_rank) are implied by dest and are not read.
+ */
+int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights,
+                         const int32_t* dest, const int32_t* send_counts,
+                         int64_t num_tokens, int num_topk, int num_ranks,
+                         int num_local_experts, int64_t num_send_capacity,
+                         int32_t* send_token_idx, int32_t* send_rank,
+                         int32_t* send_idx, float* send_w, int32_t* token_row,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Row permute into the send buffer (optionally quantizing to fp8).
+ * axolotl "torch_dispatch": dispatch (row n of the send buffer is hidden row
+ * send_token_idx[n]); NeMo "uccl_ep.buffer": Buffer.dispatch /
+ * low_latency_dispatch for the fp8 form ([.., H] float8_e4m3fn plus
+ * [.., H/128] float scales).
+ *
+ * Works token by token: hidden row t is read once and stored to every
+ * distinct row token_row[t,k] >= 0 (which must be < capacity; others are
+ * skipped).  That is exactly send_x[n] = x[send_token_idx[n]] for every
+ * written row.
+ *
+ *   x           [T,H] bf16 in
+ *   token_row   [T,K] int32 in   from ep_build_send_layout
+ *   out_dtype   EP_DTYPE_BF16: send_x [cap,H] bf16, bit-exact copies;
+ *               EP_DTYPE_FP8_E4M3: send_x [cap,H] uint8 e4m3 codes and
+ *               send_scale [cap,H/128] fp32.  Per row and group g of 128
+ *               channels: amax = max |x|, scale = fp32(amax / 448),
+ *               code = e4m3(fp32(x / scale)) rounded to nearest, ties to
+ *               even, saturating at +-448, sign kept; amax == 0 gives
+ *               scale 0 and codes 0x00.  Inputs must be finite.
+ *   send_scale  NULL for bf16.
+ */
+int ep_dispatch_permute(const void* x, int64_t num_tokens, int hidden,
+                        const int32_t* token_row, int num_topk,
+                        int64_t num_send_capacity, int out_dtype, void* send_x,
+                        float* send_scale, hipStream_t stream);
+
+/*
+ * Expert-batched layout [E_local, max_num_tokens, H].
+ * vLLM "fused_moe.prepare_finalize": BatchedPrepareAndFinalize.prepare (the
+ * buffer is zero-filled; the tokens that name local expert e in any slot take
+ * slots 0, 1, ... in ascending token order; tokens_per_expert holds the
+ * counts).
+ *
+ *   x                  [T,H] bf16 in
+ *   topk_idx           [T,K] int64 in
+ *   first_expert       global id of local expert 0 (rank * E_local)
+ *   b_x                [E_local, max_num_tokens, H] bf16 out; every row past
+ *                      an expert's count is written with zeros
+ *   tokens_per_expert  [E_local] int32 out  true counts (may exceed max;
+ *                      slots >= max_num_tokens are then dropped)
+ *   token_row          [T,K] int32 out  e*max_num_tokens + slot for local
+ *                      slots, -1 otherwise (and for dropped slots)
+ *   workspace          ep_batched_workspace_bytes(T, E_local, max) bytes
+ */
+int ep_batched_prepare(const void* x, const int64_t* topk_idx,
+                       int64_t num_tokens, int num_topk, int hidden,
+                       int first_expert, int num_local_experts,
+                       int64_t max_num_tokens, void* b_x,
+                       int32_t* tokens_per_expert, int32_t* token_row,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * Weighted combine back onto the source tokens.
+ * axolotl "torch_dispatch": combine; NeMo "uccl_ep.buffer": Buffer.combine /
+ * low_latency_combine (reduce with the top-k weights); vLLM
+ * BatchedPrepareAndFinalize.finalize; NeMo token_dispatcher
+ * TokenDispatcherConfig.moe_router_dtype (fp32 for the weighted average).
+ *
+ *   out[t,:] = bf16( sum_{k=0..K-1, r = token_row[t,k] >= 0} w[t,k] * y[r,:] )
+ * accumulated in fp32: each product is rounded to fp32, then added to the
+ * running fp32 sum (starting at +0.0) in ascending k; the sum is rounded
+ * once to bf16, to nearest with ties to even.  Rows r >= num_rows are
+ * skipped.  Tokens with no row give +0.
+ *
+ *   y             [num_rows, H] bf16 in   expert outputs (send rows, or the
+ *                                         batched buffer viewed as rows)
+ *   token_row     [T,K] int32 in
+ *   topk_weights  [T,K] fp32 in
+ *   out           [T,H] bf16 out
+ */
+int ep_combine(const void* y, int64_t num_rows, const int32_t* token_row,
+               const float* topk_weights, int64_t num_tokens, int num_topk,
+               int hidden, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPDC_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every function include/epdc.h declares,
+and rejects invalid arguments on the host before touching the GPU.  No kernel
+runs here (no GPU needed)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from combine_ep_send_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libepdc.so not built")
+
+EXPECTED = {
+    "ep_abi_version", "ep_status_string", "ep_layout_workspace_bytes",
+    "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
+    "ep_dispatch_permute", "ep_batched_prepare", "ep_combine",
+}
+
+
+def test_header_declares_the_entry_points():
+    assert set(_lib.header_functions()) == EXPECTED
+
+
+def test_library_exports_every_header_function():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _lib.header_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert EXPECTED <= exported
+
+
+def test_version_and_status_strings():
+    L = _lib.lib()
+    assert L.ep_abi_version() == 1
+    assert L.ep_status_string(0) == b"ok"
+    for s in (-1, -2, -3, -4):
+        assert L.ep_status_string(s) not in (b"ok", b"unknown status")
+    assert L.ep_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    assert L.ep_layout_workspace_bytes(16384, 32) == 256 + 64 * 32 * 8
+    assert L.ep_layout_workspace_bytes(0, 32) == 256 + 1 * 32 * 8
+    assert L.ep_layout_workspace_bytes(-1, 32) == 0
+    b = L.ep_batched_workspace_bytes(8192, 32, 8192)
+    assert b >= 256 + 32 * 32 * 8 + 32 * 8192 * 4
+
+
+# Host-side validation: every call below returns before any HIP call, because
+# an argument is rejected.  Pointers are fake but never dereferenced.
+P = ctypes.c_void_p
+A16 = P(0x10000)   # 16-byte (and 256-byte) aligned fake address
+A8 = P(0x10008)
+ODD = P(0x10002)
+
+
+def test_counts_rejects_bad_arguments():
+    L = _lib.lib()
+    f = L.ep_compute_send_counts
+    ok = dict(idx=A16, T=16, K=2, P=2, El=4, C=1)
+
+    def call(idx=A16, T=16, K=2, Pn=2, El=4, C=1, dest=A16, iir=A16, sc=A16):
+        return f(idx, T, K, Pn, El, C, dest, iir, sc, None, None, None)
+    assert call(idx=None) == _lib.EP_ERR_INVALID_ARG
+    assert call(T=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(K=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(K=17) == _lib.EP_ERR_UNSUPPORTED
+    assert call(C=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(Pn=2048) == _lib.EP_ERR_UNSUPPORTED
+    assert call(Pn=64, El=256) == _lib.EP_ERR_UNSUPPORTED     # E > 8192
+    assert call(idx=ODD) == _lib.EP_ERR_INVALID_ARG
+    assert call(T=1 << 30) == _lib.EP_ERR_UNSUPPORTED
+    assert ok
+
+
+def test_layout_rejects_bad_workspace_and_capacity():
+    L = _lib.lib()
+    f = L.ep_build_send_layout
+
+    def call(ws=A16, ws_bytes=1 << 20, cap=64, T=16):
+        return f(A16, A16, A16, A16, T, 2, 2, 4, cap, A16, A16, A16, A16, A16, ws, ws_bytes,
+                 None)
+    assert call(ws=None) == _lib.EP_ERR_WORKSPACE
+    assert call(ws_bytes=16) == _lib.EP_ERR_WORKSPACE
+    assert call(ws=A8) == _lib.EP_ERR_WORKSPACE                # not 256-aligned
+    assert call(cap=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(cap=1 << 31) == _lib.EP_ERR_UNSUPPORTED
+
+
+def test_permute_and_combine_reject_bad_rows():
+    L = _lib.lib()
+    perm = L.ep_dispatch_permute
+    assert perm(A16, 4, 100, A16, 2, 8, 0, A16, None, None) == _lib.EP_ERR_INVALID_ARG  # H%8
+    assert perm(A16, 4, 64, A16, 2, 8, 1, A16, A16, None) == _lib.EP_ERR_INVALID_ARG   # H%128 fp8
+    assert perm(A16, 4, 128, A16, 2, 8, 1, A16, None, None) == _lib.EP_ERR_INVALID_ARG  # no scale
+    assert perm(A8, 4, 64, A16, 2, 8, 0, A16, None, None) == _lib.EP_ERR_INVALID_ARG   # x align
+    assert perm(A16, 4, 64, A16, 2, 8, 5, A16, None, None) == _lib.EP_ERR_INVALID_ARG  # dtype
+    comb = L.ep_combine
+    assert comb(A16, 10, A16, A16, 4, 2, 60, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(None, 10, A16, A16, 4, 2, 64, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, A16, 4, 0, 64, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, A16, 4, 2, 64, A8, None) == _lib.EP_ERR_INVALID_ARG
+
+
+def test_batched_rejects_bad_arguments():
+    L = _lib.lib()
+    f = L.ep_batched_prepare
+
+    def call(first=0, El=4, M=8, ws=A16, ws_bytes=1 << 20):
+        return f(A16, A16, 16, 2, 64, first, El, M, A16, A16, A16, ws, ws_bytes, None)
+    assert call(first=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(El=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(El=2000) == _lib.EP_ERR_UNSUPPORTED
+    assert call(M=1 << 30) == _lib.EP_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.EP_ERR_WORKSPACE
