@@ -26,10 +26,11 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "ep_abi_version": (_I32, []),
     "ep_status_string": (ctypes.c_char_p, [_I32]),
+    "ep_counts_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
     "ep_layout_workspace_bytes": (_SZ, [_I64, _I32]),
     "ep_batched_workspace_bytes": (_SZ, [_I64, _I32, _I64]),
     "ep_compute_send_counts": (
-        _I32, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+        _I32, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_build_send_layout": (
         _I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_dispatch_permute": (_I32, [_P, _I64, _I32, _P, _I32, _I64, _I32, _P, _P, _P]),

@@ -53,6 +53,12 @@ const char* ep_status_string(int status) {
   }
 }
 
+size_t ep_counts_workspace_bytes(int64_t num_tokens, int num_ranks, int num_local_experts,
+                                 int num_chunks) {
+  if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1 || num_chunks < 1) return 0;
+  return count_ws_bytes(num_ranks, num_ranks * num_local_experts, num_chunks);
+}
+
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_bins) {
   if (num_tokens < 0 || num_bins < 1) return 0;
   return kWsHeaderBytes + scan_status_bytes(num_tokens, num_bins);
@@ -69,7 +75,8 @@ size_t ep_batched_workspace_bytes(int64_t num_tokens, int num_local_experts,
 int ep_compute_send_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
                            int num_ranks, int num_local_experts, int num_chunks, int32_t* dest,
                            uint8_t* is_in_rank, int32_t* send_counts, int32_t* tokens_per_expert,
-                           int32_t* diag, hipStream_t stream) {
+                           int32_t* diag, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   int st = check_routing(num_tokens, num_topk, num_ranks, num_local_experts);
   if (st != EP_OK) return st;
   if (num_ranks > EPDC_MAX_BINS) return EP_ERR_UNSUPPORTED;
@@ -79,6 +86,10 @@ int ep_compute_send_counts(const int64_t* topk_idx, int64_t num_tokens, int num_
       !arr_ok(is_in_rank, num_tokens * num_ranks, 4) || !arr_ok(send_counts, 1, 4) ||
       (tokens_per_expert && !aligned(tokens_per_expert, 4)) || (diag && !aligned(diag, 4)))
     return EP_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < ep_counts_workspace_bytes(num_tokens, num_ranks, num_local_experts,
+                                                  num_chunks))
+    return EP_ERR_WORKSPACE;
   CountArgs a{};
   a.topk_idx = topk_idx;
   a.T = num_tokens;
@@ -93,6 +104,8 @@ int ep_compute_send_counts(const int64_t* topk_idx, int64_t num_tokens, int num_
   a.send_counts = send_counts;
   a.tokens_per_expert = tokens_per_expert;
   a.diag = diag;
+  a.ctrl = static_cast<uint32_t*>(workspace);
+  a.accum = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
   return launch_status(launch_counts(a, stream));
 }
 
@@ -135,6 +148,7 @@ int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights, con
   a.send_rank = send_rank;
   a.send_idx = send_idx;
   a.send_w = send_w;
+  a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
   return launch_status(launch_send_layout(a, stream));
 }
 

@@ -33,6 +33,14 @@ __device__ __forceinline__ uint64_t ld_acquire(const uint64_t* p) {
 __device__ __forceinline__ void st_release(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Scan status words: the value travels inside the word, so relaxed ordering
+// is enough; agent scope keeps the access coherent across XCDs.
+__device__ __forceinline__ uint64_t ld_status(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_status(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -41,6 +49,11 @@ __device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
 }
 __device__ __forceinline__ uint32_t fetch_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Ticket and completion counters order nothing but themselves: relaxed, so
+// they do not write back or invalidate the L2 the way acq_rel would.
+__device__ __forceinline__ uint32_t fetch_add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void fetch_or(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -15,6 +15,7 @@ constexpr size_t kWsHeaderBytes = 256;
 enum : int { kCtrlTicket = 0, kCtrlDone = 1, kCtrlEpoch = 2, kCtrlError = 3 };
 constexpr uint32_t kErrLookbackGaveUp = 1u;
 
+// The layout scans work on tiles of 256 tokens (one workgroup each).
 inline int64_t num_tiles(int64_t T) { return (T + 255) / 256; }
 inline size_t scan_status_bytes(int64_t T, int bins) {
   int64_t tiles = num_tiles(T) > 0 ? num_tiles(T) : 1;
@@ -31,7 +32,13 @@ struct CountArgs {
   int32_t* send_counts;
   int32_t* tokens_per_expert;    // may be null
   int32_t* diag;                 // may be null
+  uint32_t* ctrl;                // workspace header: [0] finished workgroups
+  int32_t* accum;                // [C, P + E + 1] accumulators, zero between calls
 };
+// Count workspace: 256-byte header, then one accumulator per (chunk, bin).
+inline size_t count_ws_bytes(int P, int E, int C) {
+  return kWsHeaderBytes + size_t(C) * size_t(P + E + 1) * 4u;
+}
 hipError_t launch_counts(const CountArgs& a, hipStream_t s);
 
 struct ScanArgs {
@@ -53,6 +60,7 @@ struct ScanArgs {
   int32_t* send_rank;
   int32_t* send_idx;
   float* send_w;
+  bool vec_rows;                 // K % 4 == 0 and send_idx/send_w 16-byte aligned
   // batched layout
   int64_t first_expert;
   int64_t max_tokens;

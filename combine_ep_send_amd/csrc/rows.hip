@@ -3,9 +3,11 @@
 //
 // Every kernel gives one wavefront one row: 64 lanes move the row in 16-byte
 // pieces, so a wave covers 1 KiB per access and H = 7168 bf16 (14 KiB) is 14
-// pieces per lane.  Rows are streamed with non-temporal accesses where the
-// data is touched once.  Which rows a token touches is wave-uniform, so the
-// row indices and weights sit in scalar registers.
+// pieces per lane.  Stores of rows nobody re-reads soon are non-temporal;
+// hidden-row loads are plain loads (measured faster than non-temporal ones for
+// the token-major permute on gfx950), the combine's expert-output loads are
+// non-temporal.  Which rows a token touches is wave-uniform, so the row
+// indices and weights sit in scalar registers.
 #include "epdc_device.h"
 #include "epdc_launch.h"
 
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kBlock) void permute_bf16_kernel(RowArgs a) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int j = base + i * kWave + lane;
-      if (j < H8) v[i] = ld_stream(src + j);
+      if (j < H8) v[i] = src[j];
     }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(kBlock) void permute_fp8_kernel(RowArgs a) {
       in[it][0] = u32x4{0u, 0u, 0u, 0u};
       in[it][1] = u32x4{0u, 0u, 0u, 0u};
       if (p < H16) {
-        in[it][0] = ld_stream(src + 2 * p);
-        in[it][1] = ld_stream(src + 2 * p + 1);
+        in[it][0] = src[2 * p];
+        in[it][1] = src[2 * p + 1];
       }
     }
     u32x4 q[IT];
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void batched_fill_kernel(FillArgs a) {
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int j = base + i * kWave + lane;
-        if (j < H8) v[i] = ld_stream(src + j);
+        if (j < H8) v[i] = src[j];
       }
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
@@ -207,23 +209,31 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
   if (t >= a.T) return;
   int32_t rows[KMAX];
   float wk[KMAX];
-  bool use[KMAX];
+  bool use[KMAX];    // slot contributes
+  int from[KMAX];    // slot whose loaded row it reuses (itself if first)
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     rows[k] = 0;
     wk[k] = 0.0f;
     use[k] = false;
+    from[k] = k;
     if (k < a.K) {
       const int32_t r = a.token_row[t * a.K + k];
       rows[k] = r;
       wk[k] = a.w[t * a.K + k];
       use[k] = r >= 0 && int64_t(r) < a.R;
+#pragma unroll
+      for (int j = k - 1; j >= 0; --j)
+        if (use[j] && from[j] == j && rows[j] == r) from[k] = j;
     }
   }
   const int H8 = a.H >> 3;
   const u32x4* y = static_cast<const u32x4*>(a.y);
   u32x4* out = static_cast<u32x4*>(a.out) + t * H8;
   for (int base = 0; base < H8; base += kWave * VPL) {
+    // Every distinct row of the chunk is loaded before the first add, so the
+    // loads of all K slots are in flight together; a slot that repeats an
+    // earlier slot's row takes the registers instead of reading HBM again.
     u32x4 v[KMAX][VPL];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
@@ -231,7 +241,18 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
       for (int i = 0; i < VPL; ++i) {
         v[k][i] = u32x4{0u, 0u, 0u, 0u};
         const int j = base + i * kWave + lane;
-        if (use[k] && j < H8) v[k][i] = y[int64_t(rows[k]) * H8 + j];
+        if (use[k] && from[k] == k && j < H8) v[k][i] = ld_stream(y + int64_t(rows[k]) * H8 + j);
+      }
+    }
+#pragma unroll
+    for (int k = 1; k < KMAX; ++k) {
+      if (from[k] == k) continue;
+#pragma unroll
+      for (int j = 0; j < k; ++j) {
+        if (from[k] == j) {
+#pragma unroll
+          for (int i = 0; i < VPL; ++i) v[k][i] = v[j][i];
+        }
       }
     }
     float acc[VPL][8];
@@ -350,18 +371,31 @@ hipError_t launch_batched_fill(const FillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Vectors per lane per chunk for the combine: about 56 loads in flight per
+// lane (K rows x VPL pieces), with the row split into equal chunks.
+template <int KMAX, int VMAX>
+hipError_t launch_combine_k(const CombineArgs& a, hipStream_t s) {
+  const unsigned grid = row_grid(a.T);
+  const int need = pieces_per_lane(a.H >> 3);
+  const int chunks = (need + VMAX - 1) / VMAX;
+  const int vpl = (need + chunks - 1) / chunks;
+  if (vpl <= 1)
+    combine_kernel<KMAX, 1><<<grid, kBlock, 0, s>>>(a);
+  else if (vpl <= 2)
+    combine_kernel<KMAX, (VMAX < 2 ? VMAX : 2)><<<grid, kBlock, 0, s>>>(a);
+  else if (vpl <= 4)
+    combine_kernel<KMAX, (VMAX < 4 ? VMAX : 4)><<<grid, kBlock, 0, s>>>(a);
+  else
+    combine_kernel<KMAX, VMAX><<<grid, kBlock, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const unsigned grid = row_grid(a.T);
-  if (a.K <= 2)
-    combine_kernel<2, 8><<<grid, kBlock, 0, s>>>(a);
-  else if (a.K <= 4)
-    combine_kernel<4, 4><<<grid, kBlock, 0, s>>>(a);
-  else if (a.K <= 8)
-    combine_kernel<8, 2><<<grid, kBlock, 0, s>>>(a);
-  else
-    combine_kernel<16, 1><<<grid, kBlock, 0, s>>>(a);
-  return hipGetLastError();
+  if (a.K <= 2) return launch_combine_k<2, 16>(a, s);
+  if (a.K <= 4) return launch_combine_k<4, 14>(a, s);
+  if (a.K <= 8) return launch_combine_k<8, 7>(a, s);
+  return launch_combine_k<16, 4>(a, s);
 }
 
 }  // namespace epdc

@@ -4,16 +4,23 @@
 // Counts (axolotl "torch_dispatch": compute_send_counts; NeMo
 // "uccl_ep.buffer": Buffer.get_dispatch_layout): one thread per token decodes
 // its K slots; destination membership is counted per wave with one ballot per
-// destination bin and a popcount, experts with LDS atomics; each workgroup
-// then adds its LDS histogram to the global counts with one atomic per bin.
+// destination bin and a popcount, experts with LDS atomics.  Each workgroup
+// adds its non-zero LDS bins into accumulators in the workspace; the
+// workgroup that finishes last copies them out and clears them, so the call
+// is one launch and leaves the workspace zeroed for the next call.
 //
 // Layouts (axolotl build_send_layout; vLLM BatchedPrepareAndFinalize.prepare):
-// a single-pass scan with decoupled lookback.  Workgroups take tiles of 256
-// tokens from an atomic ticket (so every tile a workgroup waits on belongs to
-// a workgroup that is already running), rank their tokens inside each bin with
-// ballots, publish the tile's per-bin aggregate, then walk back over earlier
-// tiles' status words until an inclusive prefix is found.  The status words
-// carry the call's epoch, so the workspace never needs clearing between calls.
+// a single-pass scan with decoupled lookback over tiles of 256 tokens, one
+// workgroup of 4 waves per tile.  Tiles are taken from an atomic ticket, so
+// every tile a workgroup waits on belongs to one that is already running.
+// Each wave ranks its tokens inside each bin with a ballot and a popcount; the
+// workgroup publishes the tile's per-bin aggregate, looks back over earlier
+// tiles (64 at a time, one lane per tile), publishes its inclusive prefix,
+// then scatters bin by bin so that each store writes one contiguous run of
+// rows.  Status words carry the call's epoch, so the workspace never needs
+// clearing between calls.  The code is kept compact on purpose: a fully
+// unrolled lookback grows the kernel past the instruction cache, and then
+// instruction fetch, not memory, sets its duration.
 #include "epdc_device.h"
 #include "epdc_launch.h"
 
@@ -21,30 +28,27 @@ namespace epdc {
 
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 22;   // sleeps per lookback step (~0.1 s)
+constexpr uint32_t kSpinLimit = 1u << 22;   // sleeps per lookback window (~0.1 s)
+constexpr int kLookGroup = 8;               // bins whose lookback loads a wave overlaps
 
-__global__ __launch_bounds__(kBlock) void zero3_kernel(int32_t* a, int64_t na, int32_t* b,
-                                                       int64_t nb, int32_t* c, int64_t nc) {
-  const int64_t i0 = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-  const int64_t step = int64_t(gridDim.x) * kBlock;
-  for (int64_t i = i0; i < na; i += step) a[i] = 0;
-  for (int64_t i = i0; i < nb; i += step) b[i] = 0;
-  for (int64_t i = i0; i < nc; i += step) c[i] = 0;
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 // ---------------------------------------------------------------------------
-// Counts.  Grid (tiles per chunk, C); the block of chunk c covers tokens
-// [c*chunk + bx*256, ...) clipped to the chunk, so no block spans chunks.
+// Counts.  Grid (tiles per chunk, C); the workgroup of chunk c covers tokens
+// [c*chunk + bx*256, ...) clipped to the chunk, so none spans two chunks.
 // ---------------------------------------------------------------------------
 template <int KMAX>
 __global__ __launch_bounds__(kBlock) void counts_kernel(CountArgs a) {
   extern __shared__ int32_t s_hist[];  // [P] destinations, [E] experts, [1] bad ids
+  __shared__ bool s_last;
   const int c = blockIdx.y;
   const int64_t cs = int64_t(c) * a.chunk;
   const int64_t ce = (c == a.C - 1) ? a.T : cs + a.chunk;
-  const int64_t t0 = cs + int64_t(blockIdx.x) * kTile;
-  if (t0 >= ce) return;  // the whole workgroup is past its chunk
-
+  const int64_t t0 = cs + int64_t(blockIdx.x) * kBlock;
   const bool want_e = a.tokens_per_expert != nullptr;
   const int n_hist = a.P + (want_e ? a.E : 0) + 1;
   for (int i = threadIdx.x; i < n_hist; i += kBlock) s_hist[i] = 0;
@@ -109,20 +113,45 @@ __global__ __launch_bounds__(kBlock) void counts_kernel(CountArgs a) {
   if (bad) atomicAdd(&s_hist[n_hist - 1], bad);
   __syncthreads();
 
+  int32_t* acc = a.accum + int64_t(c) * n_hist;
   for (int i = threadIdx.x; i < n_hist; i += kBlock) {
     const int v = s_hist[i];
-    if (v == 0) continue;
-    if (i < a.P)
-      atomicAdd(&a.send_counts[int64_t(c) * a.P + i], v);
-    else if (i < n_hist - 1)
-      atomicAdd(&a.tokens_per_expert[int64_t(c) * a.E + (i - a.P)], v);
-    else if (a.diag)
-      atomicAdd(a.diag, v);
+    if (v != 0) atomicAdd(&acc[i], v);
   }
+  // Wait until this thread's adds are performed, then count the workgroup
+  // done.  The accumulators are only touched by device-scope atomics, so no
+  // cache writeback is needed to publish them.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = fetch_add_relaxed(&a.ctrl[0], 1u) == gridDim.x * gridDim.y - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  // Last workgroup: copy the accumulators out and clear them for the next call.
+  uint32_t* accu = reinterpret_cast<uint32_t*>(a.accum);
+  for (int64_t i = threadIdx.x; i < int64_t(a.C) * n_hist; i += kBlock) {
+    const int cc = int(i / n_hist);
+    const int bin = int(i - int64_t(cc) * n_hist);
+    const int v = int(ld_relaxed(accu + i));
+    if (bin < a.P)
+      a.send_counts[int64_t(cc) * a.P + bin] = v;
+    else if (bin < n_hist - 1)
+      a.tokens_per_expert[int64_t(cc) * a.E + (bin - a.P)] = v;
+  }
+  if (a.diag && threadIdx.x == 0) {
+    uint32_t sum = 0;
+    for (int cc = 0; cc < a.C; ++cc) sum += ld_relaxed(accu + int64_t(cc) * n_hist + n_hist - 1);
+    a.diag[0] = int(sum);
+  }
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < int64_t(a.C) * n_hist; i += kBlock) st_relaxed(accu + i, 0u);
+  if (threadIdx.x == 0) st_relaxed(&a.ctrl[0], 0u);
 }
 
 // ---------------------------------------------------------------------------
-// Single-pass scan + stable scatter (send layout or batched layout).
+// Single-pass scan + stable scatter (send layout or batched layout).  One
+// workgroup of 4 waves per tile of 256 tokens, one token per thread.
 // ---------------------------------------------------------------------------
 enum { kModeSend = 0, kModeBatched = 1 };
 
@@ -141,12 +170,13 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
   const int lane = lane_id();
   const int wave = wave_id();
   if (tid == 0) {
-    s_tile = fetch_add(&a.ctrl[kCtrlTicket], 1u);
+    s_tile = fetch_add_relaxed(&a.ctrl[kCtrlTicket], 1u);
     s_epoch = ld_relaxed(&a.ctrl[kCtrlEpoch]);
   }
   __syncthreads();
   const uint32_t tile = s_tile;
   const uint32_t epoch = s_epoch;
+  const uint32_t tiles = gridDim.x;
   const int64_t t = int64_t(tile) * kTile + tid;
   const bool valid = t < a.T;
 
@@ -173,7 +203,7 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
     }
   }
 
-  // Per-wave ballot of every bin; lane j keeps the ballot of bin w0 + j.
+  // Ballot of every bin per wave; lane j keeps the ballot of bin w0 + j.
   for (int w0 = 0; w0 < nb; w0 += kWave) {
     uint64_t m = 0;
 #pragma unroll
@@ -187,24 +217,8 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
     }
     if (lane < nwin) s_bal[wave * nb + w0 + lane] = mine;
   }
-  __syncthreads();
-
-  // Tile count per bin, exclusive offsets of the waves, and publication of
-  // the tile's aggregate (tile 0 publishes its inclusive prefix directly).
-  for (int b = tid; b < nb; b += kBlock) {
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-      s_woff[w * nb + b] = run;
-      run += int(__popcll(s_bal[w * nb + b]));
-    }
-    s_cnt[b] = run;
-    st_release(&a.status[size_t(tile) * nb + b],
-               pack_status(epoch, tile == 0 ? kFlagPrefix : kFlagAggregate, uint32_t(run)));
-  }
-
   // Segment starts of the send layout: exclusive scan of send_counts.
-  if (MODE == kModeSend && wave == 0) {
+  if (MODE == kModeSend && wave == kWavesPerBlock - 1) {
     int carry = 0;
     for (int b0 = 0; b0 < nb; b0 += kWave) {
       const int b = b0 + lane;
@@ -219,39 +233,93 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
       carry += __shfl(incl, kWave - 1);
     }
   }
+  __syncthreads();
 
-  // Decoupled lookback: one thread per bin sums earlier tiles' aggregates
-  // until it meets an inclusive prefix, then publishes its own prefix.
+  // Tile count per bin and the waves' exclusive offsets; publish the tile's
+  // aggregate (tile 0 publishes its inclusive prefix directly).
   for (int b = tid; b < nb; b += kBlock) {
-    uint32_t excl = 0;
-    if (tile > 0) {
-      int64_t j = int64_t(tile) - 1;
-      uint32_t spins = 0;
-      while (true) {
-        const uint64_t w = ld_acquire(&a.status[size_t(j) * nb + b]);
-        const uint32_t f = status_flag(w);
-        if (status_epoch(w) != epoch || f == kFlagNone) {
-          if (++spins > kSpinLimit) {
-            fetch_or(&a.ctrl[kCtrlError], kErrLookbackGaveUp);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        spins = 0;
-        excl += status_value(w);
-        if (f == kFlagPrefix || j == 0) break;
-        --j;
-      }
-      st_release(&a.status[size_t(tile) * nb + b],
-                 pack_status(epoch, kFlagPrefix, excl + uint32_t(s_cnt[b])));
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      s_woff[w * nb + b] = run;
+      run += int(__popcll(s_bal[w * nb + b]));
     }
-    s_excl[b] = int(excl);
+    s_cnt[b] = run;
+    st_status(&a.status[size_t(b) * tiles + tile],
+              pack_status(epoch, tile == 0 ? kFlagPrefix : kFlagAggregate, uint32_t(run)));
   }
   __syncthreads();
 
-  // Stable scatter: a lane's rank inside bin b is the popcount of the lower
-  // lanes in its wave's ballot, plus the earlier waves and tiles.
+  // Decoupled lookback; the waves share the bins (wave w takes bins w, w+4,
+  // ...), kLookGroup at a time.  For one bin, lane j reads the status word of
+  // tile (base - j), so 64 predecessors arrive in one coalesced load; the
+  // window adds aggregates up to the nearest inclusive prefix or moves 64
+  // tiles further back.
+  for (int g0 = wave; g0 < nb; g0 += kWavesPerBlock * kLookGroup) {
+    uint32_t excl[kLookGroup];
+    int64_t base[kLookGroup];
+    bool done[kLookGroup];
+#pragma unroll
+    for (int g = 0; g < kLookGroup; ++g) {
+      done[g] = g0 + kWavesPerBlock * g >= nb || tile == 0;
+      excl[g] = 0;
+      base[g] = int64_t(tile) - 1;
+    }
+    uint32_t spins = 0;
+    while (true) {
+      uint64_t w[kLookGroup];
+#pragma unroll
+      for (int g = 0; g < kLookGroup; ++g) {
+        const int64_t j = base[g] - lane;
+        w[g] = pack_status(epoch, kFlagPrefix, 0u);
+        if (!done[g] && j >= 0)
+          w[g] = ld_status(&a.status[size_t(g0 + kWavesPerBlock * g) * tiles + size_t(j)]);
+      }
+      bool pending = false, waiting = false;
+#pragma unroll
+      for (int g = 0; g < kLookGroup; ++g) {
+        if (done[g]) continue;
+        const uint32_t f = status_epoch(w[g]) == epoch ? status_flag(w[g]) : kFlagNone;
+        const uint64_t pm = ballot(f == kFlagPrefix);
+        const uint64_t xm = ballot(f == kFlagNone);
+        const int fp = pm ? int(__builtin_ctzll(pm)) : kWave;          // nearest prefix
+        const uint64_t upto = fp >= kWave - 1 ? ~uint64_t(0) : ((uint64_t(2) << fp) - 1);
+        if (xm & upto) {                       // a tile in the window has not published
+          pending = waiting = true;
+          continue;
+        }
+        excl[g] += wave_sum(lane <= fp ? status_value(w[g]) : 0u);
+        if (pm) {
+          done[g] = true;
+        } else {
+          base[g] -= kWave;
+          pending = true;
+        }
+      }
+      if (!pending) break;
+      if (waiting) {
+        if (++spins > kSpinLimit) {
+          if (lane == 0) fetch_or(&a.ctrl[kCtrlError], kErrLookbackGaveUp);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kLookGroup; ++g) {
+      const int b = g0 + kWavesPerBlock * g;
+      if (b < nb && lane == 0) {
+        if (tile > 0)
+          st_status(&a.status[size_t(b) * tiles + tile],
+                    pack_status(epoch, kFlagPrefix, excl[g] + uint32_t(s_cnt[b])));
+        s_excl[b] = int(excl[g]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Row of every routed slot: segment start + earlier tiles + earlier waves
+  // + lower lanes of this wave that share the bin.
   const uint64_t lt = lanemask_lt();
   int32_t rowk[KMAX];
 #pragma unroll
@@ -269,48 +337,71 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    if (rowk[k] < 0) continue;
-    bool first = true;
-#pragma unroll
-    for (int j = 0; j < k; ++j)
-      if (bin[j] == bin[k]) first = false;
-    if (!first) continue;
-    const int32_t n = rowk[k];
-    const int b = bin[k];
-    if (MODE == kModeSend) {
-      a.send_token_idx[n] = int32_t(t);
-      a.send_rank[n] = b;
-      const int64_t ob = int64_t(b) * a.E_local;
-#pragma unroll
-      for (int kk = 0; kk < KMAX; ++kk) {
-        if (kk < a.K) {
-          const bool own = bin[kk] == b;
-          a.send_idx[int64_t(n) * a.K + kk] = own ? int32_t(ids[kk] - ob) : -1;
-          a.send_w[int64_t(n) * a.K + kk] = own ? wts[kk] : 0.0f;
-        }
-      }
-    } else {
-      a.slot_token[n] = int32_t(t);
-    }
-  }
   if (valid) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if (k < a.K) a.token_row[t * a.K + k] = rowk[k];
   }
 
+  // Scatter bin by bin: within a wave the members of bin b hold consecutive
+  // rows, so every store below writes one contiguous run.
+  for (int b = 0; b < nb; ++b) {
+    const uint64_t bal = s_bal[wave * nb + b];
+    if (!((bal >> lane) & 1u)) continue;
+    int32_t n = -1;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (bin[k] == b) n = rowk[k];
+    if (n < 0) continue;
+    if (MODE == kModeSend) {
+      a.send_token_idx[n] = int32_t(t);
+      a.send_rank[n] = b;
+      const int64_t ob = int64_t(b) * a.E_local;
+      int32_t* irow = a.send_idx + int64_t(n) * a.K;
+      float* wrow = a.send_w + int64_t(n) * a.K;
+#pragma unroll
+      for (int kk = 0; kk < KMAX; kk += 4) {
+        if (kk >= a.K) break;
+        int32_t iv[4];
+        float wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool own = bin[kk + q] == b;
+          iv[q] = own ? int32_t(ids[kk + q] - ob) : -1;
+          wv[q] = own ? wts[kk + q] : 0.0f;
+        }
+        if (a.vec_rows) {
+          *reinterpret_cast<u32x4*>(irow + kk) =
+              u32x4{uint32_t(iv[0]), uint32_t(iv[1]), uint32_t(iv[2]), uint32_t(iv[3])};
+          *reinterpret_cast<u32x4*>(wrow + kk) =
+              u32x4{__float_as_uint(wv[0]), __float_as_uint(wv[1]), __float_as_uint(wv[2]),
+                    __float_as_uint(wv[3])};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (kk + q < a.K) {
+              irow[kk + q] = iv[q];
+              wrow[kk + q] = wv[q];
+            }
+          }
+        }
+      }
+    } else {
+      a.slot_token[n] = int32_t(t);
+    }
+  }
+
   // The last tile holds the totals of the batched layout.
-  if (MODE == kModeBatched && tile == gridDim.x - 1) {
+  if (MODE == kModeBatched && tile == tiles - 1) {
     for (int b = tid; b < nb; b += kBlock) a.tokens_per_expert[b] = s_excl[b] + s_cnt[b];
   }
 
-  // The workgroup that finishes last rearms the workspace for the next call.
+  // The workgroup that finishes last rearms the workspace for the next call
+  // (the next launch sees these stores: kernel boundaries order memory).
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = fetch_add(&a.ctrl[kCtrlDone], 1u);
-    if (prev == gridDim.x - 1) {
+    const uint32_t prev = fetch_add_relaxed(&a.ctrl[kCtrlDone], 1u);
+    if (prev == tiles - 1) {
       st_relaxed(&a.ctrl[kCtrlTicket], 0u);
       st_relaxed(&a.ctrl[kCtrlDone], 0u);
       st_relaxed(&a.ctrl[kCtrlEpoch], epoch + 1u);
@@ -337,21 +428,10 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s, unsigned grid) {
 }  // namespace
 
 hipError_t launch_counts(const CountArgs& a, hipStream_t s) {
-  const int64_t n_sc = int64_t(a.C) * a.P;
-  const int64_t n_te = a.tokens_per_expert ? int64_t(a.C) * a.E : 0;
-  const int64_t n_dg = a.diag ? 1 : 0;
-  const int64_t most = n_sc > n_te ? n_sc : n_te;
-  unsigned zgrid = unsigned((most + kBlock - 1) / kBlock);
-  if (zgrid < 1) zgrid = 1;
-  if (zgrid > 1024) zgrid = 1024;
-  zero3_kernel<<<zgrid, kBlock, 0, s>>>(a.send_counts, n_sc, a.tokens_per_expert, n_te, a.diag,
-                                       n_dg);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.T == 0) return err;
-
   const int64_t longest = a.T - int64_t(a.C - 1) * a.chunk;  // the last chunk
-  const unsigned gx = unsigned((longest + kTile - 1) / kTile);
-  const dim3 grid(gx, unsigned(a.C));
+  int64_t gx = (longest + kBlock - 1) / kBlock;
+  if (gx < 1) gx = 1;              // empty input: one workgroup still writes zeros
+  const dim3 grid(unsigned(gx), unsigned(a.C));
   const size_t smem = size_t(a.P + (a.tokens_per_expert ? a.E : 0) + 1) * 4;
   if (a.K <= 4)
     counts_kernel<4><<<grid, kBlock, smem, s>>>(a);
@@ -368,7 +448,7 @@ hipError_t launch_send_layout(const ScanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_batched_scan(const ScanArgs& a, hipStream_t s) {
-  // At least one workgroup, so that an empty batch still reports zero counts.
+  // At least one tile, so that an empty batch still reports zero counts.
   const int64_t tiles = num_tiles(a.T) > 0 ? num_tiles(a.T) : 1;
   return launch_scan<kModeBatched>(a, s, unsigned(tiles));
 }

@@ -23,6 +23,7 @@ __all__ = [
     "ep_dispatch_permute",
     "ep_batched_prepare",
     "ep_combine",
+    "ep_counts_workspace_bytes",
     "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes",
     "workspace_for",
@@ -73,6 +74,12 @@ def _shape(t: torch.Tensor, name: str, shape) -> None:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def ep_counts_workspace_bytes(num_tokens: int, num_ranks: int, num_local_experts: int,
+                              num_chunks: int = 1) -> int:
+    return int(lib().ep_counts_workspace_bytes(int(num_tokens), int(num_ranks),
+                                               int(num_local_experts), int(num_chunks)))
+
+
 def ep_layout_workspace_bytes(num_tokens: int, num_bins: int) -> int:
     return int(lib().ep_layout_workspace_bytes(int(num_tokens), int(num_bins)))
 
@@ -85,13 +92,16 @@ def ep_batched_workspace_bytes(num_tokens: int, num_local_experts: int, max_num_
 _WORKSPACES = {}
 
 
-def workspace_for(nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
-    """A zero-initialised scan workspace of at least ``nbytes``, cached per
-    (device, stream).  The kernels leave it ready for the next call, so one
-    workspace serves every call enqueued on its stream."""
+def workspace_for(nbytes: int, device: torch.device, stream=None,
+                  kind: str = "scan") -> torch.Tensor:
+    """A zero-initialised workspace of at least ``nbytes``, cached per
+    (device, stream, kind).  The kernels leave it ready for the next call, so
+    one workspace serves every call of that kind enqueued on its stream.
+    ``kind`` is "counts" (ep_compute_send_counts) or "scan" (the layout and
+    batched scans, which share one protocol)."""
     s = stream if stream is not None else torch.cuda.current_stream(device)
     key = (device.index if device.index is not None else torch.cuda.current_device(),
-           s.cuda_stream)
+           s.cuda_stream, kind)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
         with torch.cuda.stream(s):
@@ -106,7 +116,8 @@ def workspace_for(nbytes: int, device: torch.device, stream=None) -> torch.Tenso
 
 def ep_compute_send_counts(topk_idx: torch.Tensor, num_ranks: int, num_local_experts: int,
                            num_chunks: int = 1, *, expert_counts: bool = True,
-                           out: Optional[Counts] = None, stream=None) -> Counts:
+                           out: Optional[Counts] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> Counts:
     _gpu(topk_idx, "topk_idx", torch.int64, 2)
     T, K = topk_idx.shape
     P, El, C = int(num_ranks), int(num_local_experts), int(num_chunks)
@@ -127,9 +138,13 @@ def ep_compute_send_counts(topk_idx: torch.Tensor, num_ranks: int, num_local_exp
         _shape(_gpu(out.tokens_per_expert, "tokens_per_expert", torch.int32),
                "tokens_per_expert", (C, E))
     _shape(_gpu(out.diag, "diag", torch.int32), "diag", (1,))
+    if workspace is None:
+        workspace = workspace_for(ep_counts_workspace_bytes(T, P, El, C), dev, stream, "counts")
+    _gpu(workspace, "workspace", torch.uint8)
     st = lib().ep_compute_send_counts(
         _vp(topk_idx), T, K, P, El, C, _vp(out.dest), _vp(out.is_in_rank), _vp(out.send_counts),
-        _vp(out.tokens_per_expert), _vp(out.diag), _stream(stream))
+        _vp(out.tokens_per_expert), _vp(out.diag), _vp(workspace), workspace.numel(),
+        _stream(stream))
     check(st, "ep_compute_send_counts")
     return out
 

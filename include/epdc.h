@@ -84,11 +84,21 @@ int ep_abi_version(void);
 const char* ep_status_string(int status);
 
 /*
+ * Bytes of workspace ep_compute_send_counts needs: a 256-byte header (uint32
+ * word [0] counts finished workgroups) followed by one int32 accumulator per
+ * (chunk, bin), P + E + 1 bins per chunk.  Zero-filled once before first use;
+ * every call clears what it used, leaving it ready for the next call; calls
+ * that may overlap in time must use different workspaces.
+ */
+size_t ep_counts_workspace_bytes(int64_t num_tokens, int num_ranks,
+                                 int num_local_experts, int num_chunks);
+
+/*
  * Bytes of workspace ep_build_send_layout needs for T tokens and P
  * destinations (its scan bins).  The workspace holds the cross-workgroup
  * scan state: a 256-byte header (uint32 words: [0] tile ticket, [1] finished
  * tiles, [2] call epoch, [3] error flags: bit 0 = a lookback wait gave up)
- * followed by one 64-bit status word per (tile of 256 tokens, bin).
+ * followed by one 64-bit status word per (bin, tile of 256 tokens).
  * It must be zero-filled once before its first use; every call leaves it
  * ready for the next call.  Calls that may overlap in time (different
  * streams) must use different workspaces.
@@ -118,13 +128,16 @@ size_t ep_batched_workspace_bytes(int64_t num_tokens, int num_local_experts,
  *   tokens_per_expert  [C,E] int32 out  routed slots naming e in chunk c
  *                                       (may be NULL)
  *   diag               [1]   int32 out  ids outside [-1, E) (may be NULL)
- * All outputs are fully overwritten (counts are cleared by the call).
+ *   workspace          ep_counts_workspace_bytes(T, P, E_local, C) bytes
+ * All outputs are fully overwritten (integer sums, so the result does not
+ * depend on the order in which workgroups add their histograms).
  */
 int ep_compute_send_counts(const int64_t* topk_idx, int64_t num_tokens,
                            int num_topk, int num_ranks, int num_local_experts,
                            int num_chunks, int32_t* dest, uint8_t* is_in_rank,
                            int32_t* send_counts, int32_t* tokens_per_expert,
-                           int32_t* diag, hipStream_t stream);
+                           int32_t* diag, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Stable destination-major send layout.

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libepdc.so not built")
 
 EXPECTED = {
-    "ep_abi_version", "ep_status_string", "ep_layout_workspace_bytes",
+    "ep_abi_version", "ep_status_string", "ep_counts_workspace_bytes", "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
     "ep_dispatch_permute", "ep_batched_prepare", "ep_combine",
 }
@@ -45,6 +45,9 @@ def test_version_and_status_strings():
 
 def test_workspace_sizes():
     L = _lib.lib()
+    assert L.ep_counts_workspace_bytes(16384, 32, 8, 1) == 256 + (32 + 256 + 1) * 4
+    assert L.ep_counts_workspace_bytes(32768, 32, 8, 4) == 256 + 4 * (32 + 256 + 1) * 4
+    assert L.ep_counts_workspace_bytes(0, 2, 4, 3) == 256 + 3 * (2 + 8 + 1) * 4
     assert L.ep_layout_workspace_bytes(16384, 32) == 256 + 64 * 32 * 8
     assert L.ep_layout_workspace_bytes(0, 32) == 256 + 1 * 32 * 8
     assert L.ep_layout_workspace_bytes(-1, 32) == 0
@@ -65,8 +68,9 @@ def test_counts_rejects_bad_arguments():
     f = L.ep_compute_send_counts
     ok = dict(idx=A16, T=16, K=2, P=2, El=4, C=1)
 
-    def call(idx=A16, T=16, K=2, Pn=2, El=4, C=1, dest=A16, iir=A16, sc=A16):
-        return f(idx, T, K, Pn, El, C, dest, iir, sc, None, None, None)
+    def call(idx=A16, T=16, K=2, Pn=2, El=4, C=1, dest=A16, iir=A16, sc=A16, ws=A16,
+             ws_bytes=1 << 20):
+        return f(idx, T, K, Pn, El, C, dest, iir, sc, None, None, ws, ws_bytes, None)
     assert call(idx=None) == _lib.EP_ERR_INVALID_ARG
     assert call(T=-1) == _lib.EP_ERR_INVALID_ARG
     assert call(K=0) == _lib.EP_ERR_INVALID_ARG
@@ -76,6 +80,8 @@ def test_counts_rejects_bad_arguments():
     assert call(Pn=64, El=256) == _lib.EP_ERR_UNSUPPORTED     # E > 8192
     assert call(idx=ODD) == _lib.EP_ERR_INVALID_ARG
     assert call(T=1 << 30) == _lib.EP_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.EP_ERR_WORKSPACE
+    assert call(ws_bytes=64) == _lib.EP_ERR_WORKSPACE
     assert ok
 
 
