@@ -12,6 +12,10 @@ routing, with inputs already resident in HBM:
 The identity expert sits between dispatch and combine: combine reads the send
 rows themselves (bf16), or the dequantized fp8 rows prepared before timing.
 
+Every step, warm-up included, follows a 512 MiB scratch write (outside the
+step's events) that clears the 256 MB Infinity Cache, so each step reads its
+inputs from HBM; ``--back-to-back`` times K uninterrupted steps instead.
+
 Prints ONE JSON line.  ``value`` is algorithmic HBM bytes per step / step
 time (GB/s); tokens/s and the fraction of the 8 TB/s HBM peak ride along.
 ``roofline`` describes the dominant kernel, timed with HIP events on its own
@@ -301,17 +305,31 @@ def cpu_baseline(s, budget_tokens):
     }
 
 
-def traffic_from_profiles(kernel_name, source_digest, launches_per_step):
-    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE,
-    if a committed summary exists for the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.json")
+KERNEL_SOURCES = ("rows.hip", "epdc_device.h", "epdc_launch.h")
+
+
+def kernel_source_digest():
+    """SHA-256 over the sources of the row kernels (the measured traffic is
+    only valid for the code it was measured on)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "combine_ep_send_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(workload, kernel_name, source_digest):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (each scaled by its reading for a plain 1 GiB copy), if a committed
+    summary exists for this workload, kernel and kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{kernel_name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_sha256") != source_digest:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
 def main():
@@ -323,6 +341,14 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the CPU-oracle sample (default: sized for ~15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--back-to-back", action="store_true",
+                    help="run the timed steps back to back under one pair of events, "
+                         "without clearing the Infinity Cache between steps (by default "
+                         "every step, warm-up included, follows a 512 MiB scratch write "
+                         "outside its events, so no step finds its inputs in the cache)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run five plain 1 GiB device copies (the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -338,6 +364,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}), flush=True)
+        return 0
     ep.lib()                                   # fail loudly if the library is missing
     s = spec(args.workload)
     log(f"[bench] workload {s.name}: T={s.T} H={s.H} E={s.E} K={s.K} P={s.P} "
@@ -359,25 +396,43 @@ def main():
     total_bytes = int(sum(kbytes.values()))
     log(f"[bench] setup done: {info}; algorithmic bytes/step = {total_bytes / 1e9:.4f} GB")
 
+    main_stream = torch.cuda.current_stream()
+    # 512 MiB of scratch: twice the Infinity Cache, so writing it evicts every
+    # line a previous step left there.
+    scratch = (torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+               if not args.back_to_back else None)
     for _ in range(args.warmup):
+        if scratch is not None:
+            scratch.zero_()
         step()
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
-
-    # Timed region: K whole steps between two events on the main stream (the
-    # chunked workload joins its side streams back into it every step).
-    main_stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record(main_stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(main_stream)
-    torch.cuda.synchronize()
+    if scratch is None:
+        # Timed region: K whole steps between two events on the main stream
+        # (the chunked workload joins its side streams back into it every step).
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(main_stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(main_stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+    else:
+        # Each step between its own events, the cache-clearing write before it.
+        evs = []
+        for _ in range(args.steps):
+            scratch.zero_()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(main_stream)
+            step()
+            e1.record(main_stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     wall = time.perf_counter() - w0
-    ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {args.steps} timed steps: {ms:.4f} ms/step (events), "
         f"{1000 * wall / args.steps:.4f} ms/step (wall)")
 
@@ -386,16 +441,15 @@ def main():
     # cost a few microseconds each, so this pass is kept out of the step time.)
     timer = Timer(torch)
     for _ in range(args.steps):
+        if scratch is not None:
+            scratch.zero_()
         step(timer)
     torch.cuda.synchronize()
     kern_us = timer.averages_us()
     per_launch = info.get("per_launch_bytes", kbytes)
     dom = max((k for k in kern_us if k != "counts" and k != "layout"), key=lambda k: kern_us[k])
     dom_gbs = per_launch[dom] / (kern_us[dom] * 1e-6) / 1e9
-    src = os.path.join(ROOT, "combine_ep_send_amd", "csrc", "rows.hip")
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    traffic = traffic_from_profiles(dom, digest, 1)
+    trec = traffic_from_profiles(s.name, dom, kernel_source_digest())
 
     gbs = total_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -416,12 +470,16 @@ def main():
             "routing": s.routing + (f"(s={s.zipf_s})" if s.routing == "zipf" else ""),
             "unrouted_frac": s.unrouted_frac, "layout": s.layout, "chunks": s.chunks,
             "streams": s.streams, "seed": s.seed, "parallelism": "single GPU",
+            "mall_flush_between_steps": not args.back_to_back,
             **{k: v for k, v in info.items() if k != "per_launch_bytes"},
         },
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "alg_bytes_per_step": total_bytes,
         "wall_ms_per_step": round(1000 * wall / args.steps, 5),
+        "step_timing": ("one event pair around K back-to-back steps" if args.back_to_back else
+                        "events around each step; a 512 MiB cache-clearing write precedes "
+                        "every step, outside its events (wall time includes it)"),
         "kernel_avg_us": {k: round(v, 3) for k, v in kern_us.items()},
         "roofline": {
             "kernel": dom,
@@ -430,7 +488,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": (trec["read_bytes_per_launch"] + trec["write_bytes_per_launch"]
+                        if trec else None),
+            "traffic_read_write": ([trec["read_bytes_per_launch"], trec["write_bytes_per_launch"]]
+                                   if trec else None),
             "alg_bytes_per_launch": int(per_launch[dom]),
             "avg_launch_us": round(kern_us[dom], 3),
         },
