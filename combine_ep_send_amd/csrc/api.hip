@@ -67,9 +67,7 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_bins) {
 size_t ep_batched_workspace_bytes(int64_t num_tokens, int num_local_experts,
                                   int64_t max_num_tokens) {
   if (num_tokens < 0 || num_local_experts < 1 || max_num_tokens < 0) return 0;
-  size_t b = kWsHeaderBytes + scan_status_bytes(num_tokens, num_local_experts);
-  b = (b + 255) & ~size_t(255);
-  return b + size_t(num_local_experts) * size_t(max_num_tokens) * 4u;
+  return kWsHeaderBytes + scan_status_bytes(num_tokens, num_local_experts);
 }
 
 int ep_compute_send_counts(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
@@ -199,10 +197,9 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_token
   if (!workspace || !aligned(workspace, 256) ||
       workspace_bytes < ep_batched_workspace_bytes(num_tokens, num_local_experts, max_num_tokens))
     return EP_ERR_WORKSPACE;
-  size_t map_off = kWsHeaderBytes + scan_status_bytes(num_tokens, num_local_experts);
-  map_off = (map_off + 255) & ~size_t(255);
-  int32_t* slot_token = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + map_off);
 
+  // 1. scan: counts, slots and token_row; 2. zeros past each count;
+  // 3. the token-major permute writes the data rows (token_row = e*max+slot).
   ScanArgs a{};
   a.topk_idx = topk_idx;
   a.T = num_tokens;
@@ -213,21 +210,27 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_token
   a.token_row = token_row;
   a.first_expert = first_expert;
   a.max_tokens = max_num_tokens;
-  a.slot_token = slot_token;
   a.tokens_per_expert = tokens_per_expert;
-  hipError_t e = launch_batched_scan(a, stream);
-  if (e != hipSuccess) return EP_ERR_LAUNCH;
+  if (launch_batched_scan(a, stream) != hipSuccess) return EP_ERR_LAUNCH;
 
-  FillArgs f{};
-  f.x = x;
-  f.T = num_tokens;
-  f.H = hidden;
-  f.slot_token = slot_token;
-  f.tokens_per_expert = tokens_per_expert;
-  f.E_local = num_local_experts;
-  f.max_tokens = max_num_tokens;
-  f.b_x = b_x;
-  return launch_status(launch_batched_fill(f, stream));
+  PadArgs z{};
+  z.tokens_per_expert = tokens_per_expert;
+  z.E_local = num_local_experts;
+  z.max_tokens = max_num_tokens;
+  z.H = hidden;
+  z.b_x = b_x;
+  if (launch_zero_pad(z, stream) != hipSuccess) return EP_ERR_LAUNCH;
+
+  RowArgs r{};
+  r.x = x;
+  r.T = num_tokens;
+  r.H = hidden;
+  r.token_row = token_row;
+  r.K = num_topk;
+  r.capacity = int64_t(num_local_experts) * max_num_tokens;
+  r.out = b_x;
+  r.out_scale = nullptr;
+  return launch_status(launch_permute_bf16(r, stream));
 }
 
 int ep_combine(const void* y, int64_t num_rows, const int32_t* token_row,

@@ -64,7 +64,6 @@ struct ScanArgs {
   // batched layout
   int64_t first_expert;
   int64_t max_tokens;
-  int32_t* slot_token;           // [E_local, max_tokens]
   int32_t* tokens_per_expert;    // [E_local]
 };
 hipError_t launch_send_layout(const ScanArgs& a, hipStream_t s);
@@ -83,17 +82,17 @@ struct RowArgs {
 hipError_t launch_permute_bf16(const RowArgs& a, hipStream_t s);
 hipError_t launch_permute_fp8(const RowArgs& a, hipStream_t s);
 
-struct FillArgs {
-  const void* x;
-  int64_t T;
-  int H;
-  const int32_t* slot_token;
-  const int32_t* tokens_per_expert;
+struct PadArgs {
+  const int32_t* tokens_per_expert;  // [E_local] counts from the batched scan
   int E_local;
   int64_t max_tokens;
-  void* b_x;
+  int H;
+  void* b_x;                         // [E_local, max_tokens, H] bf16
 };
-hipError_t launch_batched_fill(const FillArgs& a, hipStream_t s);
+hipError_t launch_zero_pad(const PadArgs& a, hipStream_t s);
+
+// Largest workgroup of the combine (one 16-byte piece per thread).
+constexpr int kMaxRowBlock = 1024;
 
 struct CombineArgs {
   const void* y;

@@ -343,9 +343,9 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
       if (k < a.K) a.token_row[t * a.K + k] = rowk[k];
   }
 
-  // Scatter bin by bin: within a wave the members of bin b hold consecutive
-  // rows, so every store below writes one contiguous run.
-  for (int b = 0; b < nb; ++b) {
+  // Send layout: scatter bin by bin; within a wave the members of bin b hold
+  // consecutive rows, so every store below writes one contiguous run.
+  for (int b = 0; MODE == kModeSend && b < nb; ++b) {
     const uint64_t bal = s_bal[wave * nb + b];
     if (!((bal >> lane) & 1u)) continue;
     int32_t n = -1;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
     for (int k = 0; k < KMAX; ++k)
       if (bin[k] == b) n = rowk[k];
     if (n < 0) continue;
-    if (MODE == kModeSend) {
+    {
       a.send_token_idx[n] = int32_t(t);
       a.send_rank[n] = b;
       const int64_t ob = int64_t(b) * a.E_local;
@@ -386,8 +386,6 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
           }
         }
       }
-    } else {
-      a.slot_token[n] = int32_t(t);
     }
   }
 

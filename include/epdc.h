@@ -107,8 +107,8 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_bins);
 
 /*
  * Bytes of workspace ep_batched_prepare needs: the scan state above with
- * E_local bins plus an int32 map [E_local, max_num_tokens] from batch slot to
- * source token.  Same zero-once / no-overlap rules.
+ * E_local bins (max_num_tokens does not change it).  Same zero-once /
+ * no-overlap rules.
  */
 size_t ep_batched_workspace_bytes(int64_t num_tokens, int num_local_experts,
                                   int64_t max_num_tokens);

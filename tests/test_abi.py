@@ -51,8 +51,9 @@ def test_workspace_sizes():
     assert L.ep_layout_workspace_bytes(16384, 32) == 256 + 64 * 32 * 8
     assert L.ep_layout_workspace_bytes(0, 32) == 256 + 1 * 32 * 8
     assert L.ep_layout_workspace_bytes(-1, 32) == 0
-    b = L.ep_batched_workspace_bytes(8192, 32, 8192)
-    assert b >= 256 + 32 * 32 * 8 + 32 * 8192 * 4
+    assert L.ep_batched_workspace_bytes(8192, 32, 8192) == 256 + 32 * 32 * 8
+    assert L.ep_batched_workspace_bytes(8192, 32, 0) == 256 + 32 * 32 * 8
+    assert L.ep_batched_workspace_bytes(8192, 0, 8192) == 0
 
 
 # Host-side validation: every call below returns before any HIP call, because
