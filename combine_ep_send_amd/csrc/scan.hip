@@ -16,8 +16,8 @@
 // Each wave ranks its tokens inside each bin with a ballot and a popcount; the
 // workgroup publishes the tile's per-bin aggregate, looks back over earlier
 // tiles (64 at a time, one lane per tile), publishes its inclusive prefix,
-// then scatters bin by bin so that each store writes one contiguous run of
-// rows.  Status words carry the call's epoch, so the workspace never needs
+// then writes each token's send rows (token-major: a thread loops over the
+// destinations of its own token).  Status words carry the call's epoch, so the workspace never needs
 // clearing between calls.  The code is kept compact on purpose: a fully
 // unrolled lookback grows the kernel past the instruction cache, and then
 // instruction fetch, not memory, sets its duration.
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kBlock) void counts_kernel(CountArgs a) {
       const int64_t v = a.topk_idx[t * a.K + k];
       if (v >= 0 && v < a.E) {
         e[k] = int(v);
-        d[k] = int(v / a.E_local);
+        d[k] = e[k] / a.E_local;
       } else if (v != -1) {
         ++bad;
       }
@@ -343,17 +343,18 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
       if (k < a.K) a.token_row[t * a.K + k] = rowk[k];
   }
 
-  // Send layout: scatter bin by bin; within a wave the members of bin b hold
-  // consecutive rows, so every store below writes one contiguous run.
-  for (int b = 0; MODE == kModeSend && b < nb; ++b) {
-    const uint64_t bal = s_bal[wave * nb + b];
-    if (!((bal >> lane) & 1u)) continue;
-    int32_t n = -1;
+  // Send layout, token-major: each thread writes the send row of every
+  // destination its token reaches (the first slot of each destination).
+  if (MODE == kModeSend) {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (bin[k] == b) n = rowk[k];
-    if (n < 0) continue;
-    {
+    for (int k = 0; k < KMAX; ++k) {
+      bool first = bin[k] >= 0 && rowk[k] >= 0;
+#pragma unroll
+      for (int j = 0; j < k; ++j)
+        if (bin[j] == bin[k]) first = false;
+      if (!first) continue;
+      const int b = bin[k];
+      const int32_t n = rowk[k];
       a.send_token_idx[n] = int32_t(t);
       a.send_rank[n] = b;
       const int64_t ob = int64_t(b) * a.E_local;
