@@ -5,7 +5,7 @@
 
 A step is one pass of the whole hot path over one batch of seeded synthetic
 routing, with inputs already resident in HBM:
-  send layouts:  counts -> send layout -> row permute -> combine
+  send layouts:  counts + send layout (one launch) -> row permute -> combine
   batched:       batched prepare (zero-padded) -> combine
   fp8 chunked:   counts (all chunks) -> per chunk, alternating 2 streams:
                  send layout -> fp8 quantize-permute -> combine
@@ -58,6 +58,11 @@ def bytes_layout(T, K, P, N):
     return (8 + 4 + 4) * T * K + 4 * P + N * (8 + 8 * K) + 4 * T * K
 
 
+def bytes_dispatch_layout(T, K, P, E, N):
+    # reads ids + weights, writes dest, is_in_rank, counts, the send rows' metadata, token_row
+    return 12 * T * K + 4 * T * K + T * P + 4 * (P + E) + N * (8 + 8 * K) + 4 * T * K
+
+
 def bytes_permute(H, U, N):
     return 2 * H * U + 2 * H * N
 
@@ -103,21 +108,16 @@ def build_send_step(torch, ep, s, d_idx, d_w, d_x):
     T, K, P, El, H = s.T, s.K, s.P, s.E_local, s.H
     cap = T * min(K, P)
     dev = d_x.device
-    counts = ep.ep_compute_send_counts(d_idx, P, El, 1)
-    lay = ep.ep_build_send_layout(d_idx, d_w, counts.dest, counts.send_counts[0], P, El, cap)
+    counts, lay = ep.ep_dispatch_layout(d_idx, d_w, P, El, cap)
     send_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ws = ep.workspace_for(ep.ep_layout_workspace_bytes(T, P), dev)
+    ws = ep.workspace_for(ep.ep_dispatch_layout_workspace_bytes(T, P, El), dev, kind="fused")
 
     def step(timer=None):
         st = torch.cuda.current_stream()
-        tk = timer.start("counts", st) if timer else None
-        ep.ep_compute_send_counts(d_idx, P, El, 1, out=counts)
-        if timer:
-            timer.stop(tk)
-            tk = timer.start("layout", st)
-        ep.ep_build_send_layout(d_idx, d_w, counts.dest, counts.send_counts[0], P, El, cap,
-                                out=lay, workspace=ws)
+        # counts + send layout in one launch (worst-case capacity, no host sync)
+        tk = timer.start("dispatch_layout", st) if timer else None
+        ep.ep_dispatch_layout(d_idx, d_w, P, El, cap, counts=counts, out=lay, workspace=ws)
         if timer:
             timer.stop(tk)
             tk = timer.start("permute", st)
@@ -134,8 +134,7 @@ def build_send_step(torch, ep, s, d_idx, d_w, d_x):
     N = int(counts.send_counts.sum().item())
     U = int(((d_idx >= 0).any(dim=1)).sum().item())
     kb = {
-        "counts": bytes_counts(T, K, P, s.E, 1),
-        "layout": bytes_layout(T, K, P, N),
+        "dispatch_layout": bytes_dispatch_layout(T, K, P, s.E, N),
         "permute": bytes_permute(H, U, N),
         "combine": bytes_combine(H, T, K, N),
     }
@@ -289,8 +288,13 @@ def cpu_baseline(s, budget_tokens):
                 y = O.dispatch_permute(x[a:b], sti)
                 nbytes += bytes_permute(H, U, N)
             O.combine(y, trow, w[a:b])
-            nbytes += bytes_layout(b - a, K, s.P, N) + bytes_combine(H, b - a, K, N)
-        nbytes += bytes_counts(T, K, s.P, s.E, s.chunks)
+            nbytes += bytes_combine(H, b - a, K, N)
+            if s.chunks > 1:
+                nbytes += bytes_layout(b - a, K, s.P, N)
+            else:        # the GPU step counts the one-launch counts + layout
+                nbytes += bytes_dispatch_layout(b - a, K, s.P, s.E, N)
+        if s.chunks > 1:
+            nbytes += bytes_counts(T, K, s.P, s.E, s.chunks)
     dt = time.perf_counter() - t0
     return {
         "value": round(nbytes / dt / 1e9, 4),
@@ -447,7 +451,8 @@ def main():
     torch.cuda.synchronize()
     kern_us = timer.averages_us()
     per_launch = info.get("per_launch_bytes", kbytes)
-    dom = max((k for k in kern_us if k != "counts" and k != "layout"), key=lambda k: kern_us[k])
+    dom = max((k for k in kern_us if k not in ("counts", "layout", "dispatch_layout")),
+              key=lambda k: kern_us[k])
     dom_gbs = per_launch[dom] / (kern_us[dom] * 1e-6) / 1e9
     trec = traffic_from_profiles(s.name, dom, kernel_source_digest())
 

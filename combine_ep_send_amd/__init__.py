@@ -30,6 +30,8 @@ from .ops import (  # noqa: F401
     ep_build_send_layout,
     ep_combine,
     ep_compute_send_counts,
+    ep_dispatch_layout,
+    ep_dispatch_layout_workspace_bytes,
     ep_counts_workspace_bytes,
     ep_dispatch_permute,
     ep_layout_workspace_bytes,

@@ -33,6 +33,10 @@ _SIGNATURES = {
         _I32, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ep_build_send_layout": (
         _I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "ep_dispatch_layout_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "ep_dispatch_layout": (
+        _I32, [_P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+               _P, _SZ, _P]),
     "ep_dispatch_permute": (_I32, [_P, _I64, _I32, _P, _I32, _I64, _I32, _P, _P, _P]),
     "ep_batched_prepare": (
         _I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),

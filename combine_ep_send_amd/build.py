@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libepdc.so")
-SOURCES = ["scan.hip", "rows.hip", "api.hip"]
+SOURCES = ["scan.hip", "fused.hip", "rows.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

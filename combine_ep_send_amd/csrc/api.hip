@@ -36,6 +36,24 @@ int check_hidden(int H, bool fp8) {
   return EP_OK;
 }
 
+int64_t fused_tiles(int64_t T) {
+  const int64_t t = (T + 255) / 256;   // tiles of 256 tokens
+  return t > 0 ? t : 1;
+}
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxFusedGroups;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 1;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +166,80 @@ int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights, con
   a.send_w = send_w;
   a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
   return launch_status(launch_send_layout(a, stream));
+}
+
+size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
+                                          int num_local_experts) {
+  if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1) return 0;
+  const int64_t groups = fused_tiles(num_tokens) < kMaxFusedGroups ? fused_tiles(num_tokens)
+                                                                    : kMaxFusedGroups;
+  const int64_t nh = int64_t(num_ranks) + int64_t(num_ranks) * num_local_experts + 1;
+  return kWsHeaderBytes + size_t(groups) * size_t(nh) * 4u;
+}
+
+int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64_t num_tokens,
+                       int num_topk, int num_ranks, int num_local_experts,
+                       int64_t num_send_capacity, int32_t* dest, uint8_t* is_in_rank,
+                       int32_t* send_counts, int32_t* tokens_per_expert, int32_t* diag,
+                       int32_t* send_token_idx, int32_t* send_rank, int32_t* send_idx,
+                       float* send_w, int32_t* token_row, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  int st = check_routing(num_tokens, num_topk, num_ranks, num_local_experts);
+  if (st != EP_OK) return st;
+  if (num_ranks > EPDC_MAX_BINS) return EP_ERR_UNSUPPORTED;
+  if (num_send_capacity < 0) return EP_ERR_INVALID_ARG;
+  if (num_send_capacity > INT32_MAX || num_send_capacity * num_topk > INT32_MAX)
+    return EP_ERR_UNSUPPORTED;
+  const int64_t TK = num_tokens * num_topk;
+  const int64_t cap = num_send_capacity;
+  if (!arr_ok(topk_idx, TK, 8) || !arr_ok(topk_weights, TK, 4) || !arr_ok(dest, TK, 4) ||
+      !arr_ok(is_in_rank, num_tokens * num_ranks, 4) || !arr_ok(send_counts, 1, 4) ||
+      !arr_ok(token_row, TK, 4) || !arr_ok(send_token_idx, cap, 4) ||
+      !arr_ok(send_rank, cap, 4) || !arr_ok(send_idx, cap, 4) || !arr_ok(send_w, cap, 4) ||
+      (tokens_per_expert && !aligned(tokens_per_expert, 4)) || (diag && !aligned(diag, 4)))
+    return EP_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < ep_dispatch_layout_workspace_bytes(num_tokens, num_ranks,
+                                                           num_local_experts))
+    return EP_ERR_WORKSPACE;
+  // Groups: one per compute unit at most, each a contiguous run of tiles.
+  const int64_t tiles = fused_tiles(num_tokens);
+  const int E = num_ranks * num_local_experts;
+  constexpr size_t kSmemLimit = 64 * 1024;
+  if (fused_smem_bytes(num_ranks, E, int((tiles + kMaxFusedGroups - 1) / kMaxFusedGroups)) >
+      kSmemLimit)
+    return EP_ERR_UNSUPPORTED;
+  int64_t gmax = device_cus();
+  if (gmax > kMaxFusedGroups) gmax = kMaxFusedGroups;
+  const int64_t per = (tiles + gmax - 1) / gmax;
+  const int64_t groups = (tiles + per - 1) / per;
+  if (fused_smem_bytes(num_ranks, E, int(per)) > kSmemLimit) return EP_ERR_UNSUPPORTED;
+
+  FusedArgs a{};
+  a.topk_idx = topk_idx;
+  a.topk_weights = topk_weights;
+  a.T = num_tokens;
+  a.K = num_topk;
+  a.P = num_ranks;
+  a.E_local = num_local_experts;
+  a.E = E;
+  a.capacity = cap;
+  a.dest = dest;
+  a.is_in_rank = is_in_rank;
+  a.send_counts = send_counts;
+  a.tokens_per_expert = tokens_per_expert;
+  a.diag = diag;
+  a.send_token_idx = send_token_idx;
+  a.send_rank = send_rank;
+  a.send_idx = send_idx;
+  a.send_w = send_w;
+  a.token_row = token_row;
+  a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
+  a.ctrl = static_cast<uint32_t*>(workspace);
+  a.rows = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
+  a.tiles = tiles;
+  a.tiles_per_group = int(per);
+  return launch_status(launch_dispatch_layout(a, unsigned(groups), stream));
 }
 
 int ep_dispatch_permute(const void* x, int64_t num_tokens, int hidden, const int32_t* token_row,

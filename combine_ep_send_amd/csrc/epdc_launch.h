@@ -69,6 +69,37 @@ struct ScanArgs {
 hipError_t launch_send_layout(const ScanArgs& a, hipStream_t s);
 hipError_t launch_batched_scan(const ScanArgs& a, hipStream_t s);
 
+struct FusedArgs {
+  const int64_t* topk_idx;
+  const float* topk_weights;
+  int64_t T;
+  int K;
+  int P;
+  int E_local;
+  int E;
+  int64_t capacity;
+  int32_t* dest;
+  uint8_t* is_in_rank;
+  int32_t* send_counts;          // [P]
+  int32_t* tokens_per_expert;    // [E] or null
+  int32_t* diag;                 // [1] or null
+  int32_t* send_token_idx;
+  int32_t* send_rank;
+  int32_t* send_idx;
+  float* send_w;
+  int32_t* token_row;
+  bool vec_rows;                 // K % 4 == 0 and send_idx/send_w 16-byte aligned
+  uint32_t* ctrl;                // workspace header: [0] arrivals, [2] barrier generation
+  uint32_t* rows;                // [groups, P + E + 1] published totals
+  int64_t tiles;                 // tiles of 256 tokens (>= 1)
+  int tiles_per_group;
+};
+// Workgroups of the fused counts + layout launch: at most one per compute
+// unit and at most kMaxFusedGroups, so that all of them are resident at once.
+constexpr int kMaxFusedGroups = 256;
+size_t fused_smem_bytes(int P, int E, int tiles_per_group);
+hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
+
 struct RowArgs {
   const void* x;
   int64_t T;

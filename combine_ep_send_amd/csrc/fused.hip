@@ -1,0 +1,361 @@
+// Counts and send layout in one launch (gfx950, wave64).
+//
+// axolotl "torch_dispatch": compute_send_counts + build_send_layout; NeMo
+// "uccl_ep.buffer": Buffer.get_dispatch_layout.  Same outputs as the two
+// separate calls, computed as reduce-then-scan with one grid-wide barrier:
+//
+//  1. Each workgroup owns a contiguous run of tiles (256 tokens each).  It
+//     decodes them (dest, is_in_rank), counts every tile's tokens per
+//     destination with per-wave ballots, histograms experts in LDS, and
+//     publishes its totals per destination / expert as one row.
+//  2. Barrier: every workgroup has published.  The grid is at most one
+//     workgroup per compute unit, so all of them are resident together.
+//  3. Each workgroup reads the rows: the destination totals give the segment
+//     starts, the rows of lower workgroups its base inside each segment.  A
+//     slice of the experts is summed by every workgroup.
+//  4. It ranks its tokens again and writes token_row and the send rows
+//     token-major.
+//
+// Against the two-call path this removes one launch and the tile-to-tile
+// lookback chain; only the barrier's round trip remains.
+#include "epdc_device.h"
+#include "epdc_launch.h"
+
+namespace epdc {
+
+namespace {
+
+constexpr uint32_t kBarrierSpinLimit = 1u << 22;   // sleeps (~0.1 s), then give up
+
+// One tile's slots: owning destination (bin), global id and weight.
+template <int KMAX>
+struct TileSlots {
+  int bin[KMAX];
+  int64_t ids[KMAX];
+  float wts[KMAX];
+  int bad;
+};
+
+template <int KMAX>
+__device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid,
+                                       TileSlots<KMAX>& s) {
+  s.bad = 0;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    s.bin[k] = -1;
+    s.ids[k] = -1;
+    s.wts[k] = 0.0f;
+    if (valid && k < a.K) {
+      const int64_t v = a.topk_idx[t * a.K + k];
+      s.ids[k] = v;
+      s.wts[k] = a.topk_weights[t * a.K + k];
+      if (v >= 0 && v < a.E)
+        s.bin[k] = int(v) / a.E_local;
+      else if (v != -1)
+        ++s.bad;
+    }
+  }
+}
+
+// Per-wave ballots of every destination for one tile: s_bal[wave*P + b].
+template <int KMAX>
+__device__ __forceinline__ void ballots(const TileSlots<KMAX>& s, int P, int wave, int lane,
+                                        uint64_t* s_bal) {
+  for (int w0 = 0; w0 < P; w0 += kWave) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (s.bin[k] >= w0 && s.bin[k] < w0 + kWave) m |= uint64_t(1) << (s.bin[k] - w0);
+    const int nwin = min(kWave, P - w0);
+    uint64_t mine = 0;
+    for (int j = 0; j < nwin; ++j) {
+      const uint64_t b = ballot((m >> j) & 1u);
+      if (lane == j) mine = b;
+    }
+    if (lane < nwin) s_bal[wave * P + w0 + lane] = mine;
+  }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int P = a.P;
+  const int nh = a.P + a.E + 1;                 // published row: P dests, E experts, bad
+  uint64_t* s_bal = reinterpret_cast<uint64_t*>(smem);                        // [4][P]
+  int32_t* s_woff = reinterpret_cast<int32_t*>(s_bal + kWavesPerBlock * P);   // [4][P]
+  int32_t* s_tcnt = s_woff + kWavesPerBlock * P;                             // [tpw][P]
+  int32_t* s_hist = s_tcnt + a.tiles_per_group * P;                          // [nh]
+  int32_t* s_tot = s_hist + nh;                                              // [P]
+  int32_t* s_base = s_tot + P;                                               // [P]
+  __shared__ uint32_t s_gen;
+  __shared__ int32_t s_bad;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int G = gridDim.x;
+  const int g = blockIdx.x;
+  const int64_t tile0 = int64_t(g) * a.tiles_per_group;
+  int64_t tile1 = tile0 + a.tiles_per_group;
+  if (tile1 > a.tiles) tile1 = a.tiles;
+  const int my_tiles = tile1 > tile0 ? int(tile1 - tile0) : 0;
+  const bool want_e = a.tokens_per_expert != nullptr;
+
+  if (tid == 0) {
+    s_gen = ld_relaxed(&a.ctrl[kCtrlEpoch]);
+    s_bad = 0;
+  }
+  for (int i = tid; i < nh; i += kBlock) s_hist[i] = 0;
+  __syncthreads();
+
+  // ---- 1. decode, count, publish ------------------------------------------
+  TileSlots<KMAX> sl;
+  for (int j = 0; j < my_tiles; ++j) {
+    const int64_t t = (tile0 + j) * kTile + tid;
+    const bool valid = t < a.T;
+    decode<KMAX>(a, t, valid, sl);
+    if (valid) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (k < a.K) a.dest[t * a.K + k] = sl.bin[k];
+      // membership row, 4 destinations per 32-bit store when P % 4 == 0
+      uint8_t* row = a.is_in_rank + t * P;
+      for (int p0 = 0; p0 < P; p0 += 4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const int d = sl.bin[k] - p0;
+          if (d >= 0 && d < 4) word |= 1u << (8 * d);
+        }
+        if ((P & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(row + p0) = word;
+        } else {
+          for (int q = 0; q < 4 && p0 + q < P; ++q) row[p0 + q] = uint8_t((word >> (8 * q)) & 1u);
+        }
+      }
+    }
+    if (want_e) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (sl.bin[k] >= 0) atomicAdd(&s_hist[P + int(sl.ids[k])], 1);
+    }
+    if (sl.bad) atomicAdd(&s_hist[nh - 1], sl.bad);
+    ballots<KMAX>(sl, P, wave, lane, s_bal);
+    __syncthreads();
+    for (int b = tid; b < P; b += kBlock) {
+      int cnt = 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) cnt += int(__popcll(s_bal[w * P + b]));
+      s_tcnt[j * P + b] = cnt;
+      s_hist[b] += cnt;
+    }
+    __syncthreads();
+  }
+  uint32_t* row_out = a.rows + int64_t(g) * nh;
+  for (int i = tid; i < nh; i += kBlock) st_relaxed(row_out + i, uint32_t(s_hist[i]));
+
+  // ---- 2. grid barrier --------------------------------------------------------
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's row stores are performed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t gen = s_gen;
+    if (fetch_add_relaxed(&a.ctrl[kCtrlTicket], 1u) == uint32_t(G - 1)) {
+      st_relaxed(&a.ctrl[kCtrlTicket], 0u);
+      st_relaxed(&a.ctrl[kCtrlEpoch], gen + 1u);
+    } else {
+      uint32_t spins = 0;
+      while (ld_relaxed(&a.ctrl[kCtrlEpoch]) == gen) {
+        if (++spins > kBarrierSpinLimit) {
+          fetch_or(&a.ctrl[kCtrlError], kErrLookbackGaveUp);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. totals, bases, expert slice -----------------------------------------
+  for (int b = tid; b < P; b += kBlock) {
+    s_tot[b] = 0;
+    s_base[b] = 0;
+  }
+  __syncthreads();
+  const uint32_t* rows_in = a.rows;
+  {
+    // (group, destination) pairs, 8 loads in flight per thread
+    const int64_t n = int64_t(G) * P;
+    for (int64_t i0 = tid; i0 < n; i0 += int64_t(kBlock) * 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + int64_t(u) * kBlock;
+        v[u] = 0u;
+        if (i < n) v[u] = ld_relaxed(rows_in + (i / P) * nh + (i % P));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + int64_t(u) * kBlock;
+        if (i < n && v[u]) {
+          const int grp = int(i / P), b = int(i % P);
+          atomicAdd(&s_tot[b], int(v[u]));
+          if (grp < g) atomicAdd(&s_base[b], int(v[u]));
+        }
+      }
+    }
+  }
+  // experts [e0, e1) of this workgroup's slice, and the bad-id total (group 0)
+  const int per_g = (a.E + G - 1) / G;
+  const int e0 = g * per_g;
+  const int e1 = min(a.E, e0 + per_g);
+  const int ne = want_e && e1 > e0 ? e1 - e0 : 0;
+  int32_t* s_etot = s_hist;            // reuse: [ne] expert totals
+  for (int i = tid; i < ne; i += kBlock) s_etot[i] = 0;
+  __syncthreads();
+  {
+    const int64_t n = int64_t(G) * ne;
+    for (int64_t i0 = tid; i0 < n; i0 += int64_t(kBlock) * 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + int64_t(u) * kBlock;
+        v[u] = 0u;
+        if (i < n) v[u] = ld_relaxed(rows_in + (i / ne) * nh + P + e0 + (i % ne));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + int64_t(u) * kBlock;
+        if (i < n && v[u]) atomicAdd(&s_etot[int(i % ne)], int(v[u]));
+      }
+    }
+  }
+  if (g == 0 && a.diag) {
+    for (int grp = tid; grp < G; grp += kBlock) {
+      const uint32_t v = ld_relaxed(rows_in + int64_t(grp) * nh + nh - 1);
+      if (v) atomicAdd(&s_bad, int(v));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < ne; i += kBlock) a.tokens_per_expert[e0 + i] = s_etot[i];
+  if (g == 0) {
+    for (int b = tid; b < P; b += kBlock) a.send_counts[b] = s_tot[b];
+    if (tid == 0 && a.diag) a.diag[0] = s_bad;
+  }
+  // Segment starts (exclusive scan of the totals) added into the bases.
+  if (wave == 0) {
+    int carry = 0;
+    for (int b0 = 0; b0 < P; b0 += kWave) {
+      const int b = b0 + lane;
+      const int v = b < P ? s_tot[b] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+      }
+      if (b < P) s_base[b] += carry + incl - v;
+      carry += __shfl(incl, kWave - 1);
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. rows and scatter ------------------------------------------------------
+  const uint64_t lt = lanemask_lt();
+  for (int j = 0; j < my_tiles; ++j) {
+    const int64_t t = (tile0 + j) * kTile + tid;
+    const bool valid = t < a.T;
+    if (my_tiles > 1) {       // a single tile's slots are still in registers
+      decode<KMAX>(a, t, valid, sl);
+      ballots<KMAX>(sl, P, wave, lane, s_bal);
+    }
+    __syncthreads();
+    for (int b = tid; b < P; b += kBlock) {
+      int run = s_base[b];
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        s_woff[w * P + b] = run;
+        run += int(__popcll(s_bal[w * P + b]));
+      }
+    }
+    __syncthreads();
+    int32_t rowk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      rowk[k] = -1;
+      const int b = sl.bin[k];
+      if (b >= 0) {
+        const int64_t n = int64_t(s_woff[wave * P + b]) + __popcll(s_bal[wave * P + b] & lt);
+        if (n < a.capacity) rowk[k] = int32_t(n);
+      }
+    }
+    if (valid) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (k < a.K) a.token_row[t * a.K + k] = rowk[k];
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      bool first = sl.bin[k] >= 0 && rowk[k] >= 0;
+#pragma unroll
+      for (int q = 0; q < k; ++q)
+        if (sl.bin[q] == sl.bin[k]) first = false;
+      if (!first) continue;
+      const int b = sl.bin[k];
+      const int32_t n = rowk[k];
+      a.send_token_idx[n] = int32_t(t);
+      a.send_rank[n] = b;
+      const int64_t ob = int64_t(b) * a.E_local;
+      int32_t* irow = a.send_idx + int64_t(n) * a.K;
+      float* wrow = a.send_w + int64_t(n) * a.K;
+#pragma unroll
+      for (int kk = 0; kk < KMAX; kk += 4) {
+        if (kk >= a.K) break;
+        int32_t iv[4];
+        float wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool own = kk + q < KMAX && sl.bin[kk + q] == b;
+          iv[q] = own ? int32_t(sl.ids[kk + q] - ob) : -1;
+          wv[q] = own ? sl.wts[kk + q] : 0.0f;
+        }
+        if (a.vec_rows) {
+          *reinterpret_cast<u32x4*>(irow + kk) =
+              u32x4{uint32_t(iv[0]), uint32_t(iv[1]), uint32_t(iv[2]), uint32_t(iv[3])};
+          *reinterpret_cast<u32x4*>(wrow + kk) =
+              u32x4{__float_as_uint(wv[0]), __float_as_uint(wv[1]), __float_as_uint(wv[2]),
+                    __float_as_uint(wv[3])};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (kk + q < a.K) {
+              irow[kk + q] = iv[q];
+              wrow[kk + q] = wv[q];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int b = tid; b < P; b += kBlock) s_base[b] += s_tcnt[j * P + b];
+  }
+}
+
+}  // namespace
+
+size_t fused_smem_bytes(int P, int E, int tiles_per_group) {
+  return size_t(P) * (kWavesPerBlock * 8 + kWavesPerBlock * 4 + 2 * 4) +
+         size_t(tiles_per_group) * P * 4 + size_t(P + E + 1) * 4;
+}
+
+hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s) {
+  const size_t smem = fused_smem_bytes(a.P, a.E, a.tiles_per_group);
+  if (a.K <= 4)
+    dispatch_layout_kernel<4><<<groups, kBlock, smem, s>>>(a);
+  else if (a.K <= 8)
+    dispatch_layout_kernel<8><<<groups, kBlock, smem, s>>>(a);
+  else
+    dispatch_layout_kernel<16><<<groups, kBlock, smem, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace epdc

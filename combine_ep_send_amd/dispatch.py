@@ -13,7 +13,7 @@ from typing import Callable, List, NamedTuple, Optional, Tuple
 import torch
 
 from .ops import (ep_batched_prepare, ep_build_send_layout, ep_combine,
-                  ep_compute_send_counts, ep_dispatch_permute)
+                  ep_compute_send_counts, ep_dispatch_layout, ep_dispatch_permute)
 
 __all__ = [
     "chunk_bounds",
@@ -93,13 +93,20 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor
     (axolotl dispatch, group=None).  Returns (recv_x, recv_idx, recv_w,
     handle); recv_x is bf16 [N,H], or (e4m3 [N,H], fp32 scales [N,H/128])
     with ``fp8``.  Without ``num_send`` the counts are copied to the host
-    once to size the buffers exactly."""
+    once to size the buffers exactly; with it (a capacity, e.g. the worst
+    case T*min(K, P)) counts and layout run as one launch."""
     T, K = topk_idx.shape
-    c = ep_compute_send_counts(topk_idx, num_ranks, num_local_experts, 1, expert_counts=False)
     if num_send is None:
+        # exact sizing: counts, one host copy, then the layout
+        c = ep_compute_send_counts(topk_idx, num_ranks, num_local_experts, 1,
+                                   expert_counts=False)
         num_send = int(to_host(c.send_counts).sum())
-    lay = ep_build_send_layout(topk_idx, topk_weights, c.dest, c.send_counts[0], num_ranks,
-                               num_local_experts, num_send)
+        lay = ep_build_send_layout(topk_idx, topk_weights, c.dest, c.send_counts[0], num_ranks,
+                                   num_local_experts, num_send)
+    else:
+        # given capacity: counts and layout in one launch, no host sync
+        c, lay = ep_dispatch_layout(topk_idx, topk_weights, num_ranks, num_local_experts,
+                                    num_send, expert_counts=False)
     recv_x = ep_dispatch_permute(x, lay.token_row, num_send, fp8=fp8)
     handle = DispatchHandle(T, lay.token_row, topk_weights, lay.send_token_idx, lay.send_rank,
                             c.send_counts[0], int(num_send))

@@ -20,6 +20,8 @@ __all__ = [
     "SendLayout",
     "ep_compute_send_counts",
     "ep_build_send_layout",
+    "ep_dispatch_layout",
+    "ep_dispatch_layout_workspace_bytes",
     "ep_dispatch_permute",
     "ep_batched_prepare",
     "ep_combine",
@@ -97,8 +99,8 @@ def workspace_for(nbytes: int, device: torch.device, stream=None,
     """A zero-initialised workspace of at least ``nbytes``, cached per
     (device, stream, kind).  The kernels leave it ready for the next call, so
     one workspace serves every call of that kind enqueued on its stream.
-    ``kind`` is "counts" (ep_compute_send_counts) or "scan" (the layout and
-    batched scans, which share one protocol)."""
+    ``kind`` is "counts" (ep_compute_send_counts), "scan" (the layout and
+    batched scans, which share one protocol) or "fused" (ep_dispatch_layout)."""
     s = stream if stream is not None else torch.cuda.current_stream(device)
     key = (device.index if device.index is not None else torch.cuda.current_device(),
            s.cuda_stream, kind)
@@ -190,6 +192,75 @@ def ep_build_send_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor,
         _vp(out.token_row), _vp(workspace), workspace.numel(), _stream(stream))
     check(st, "ep_build_send_layout")
     return out
+
+
+def ep_dispatch_layout_workspace_bytes(num_tokens: int, num_ranks: int,
+                                       num_local_experts: int) -> int:
+    return int(lib().ep_dispatch_layout_workspace_bytes(int(num_tokens), int(num_ranks),
+                                                        int(num_local_experts)))
+
+
+def ep_dispatch_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor, num_ranks: int,
+                       num_local_experts: int, num_send_capacity: int, *,
+                       expert_counts: bool = True, counts: Optional[Counts] = None,
+                       out: Optional[SendLayout] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """Counts and send layout in one launch.  Returns (Counts with C = 1,
+    SendLayout), identical to ep_compute_send_counts followed by
+    ep_build_send_layout."""
+    _gpu(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    P, El, cap = int(num_ranks), int(num_local_experts), int(num_send_capacity)
+    E = P * El
+    _shape(_gpu(topk_weights, "topk_weights", torch.float32), "topk_weights", (T, K))
+    dev = topk_idx.device
+    if counts is None:
+        counts = Counts(
+            dest=torch.empty((T, K), dtype=torch.int32, device=dev),
+            is_in_rank=torch.empty((T, P), dtype=torch.uint8, device=dev),
+            send_counts=torch.empty((1, P), dtype=torch.int32, device=dev),
+            tokens_per_expert=(torch.empty((1, E), dtype=torch.int32, device=dev)
+                               if expert_counts else None),
+            diag=torch.empty(1, dtype=torch.int32, device=dev))
+    _shape(_gpu(counts.dest, "dest", torch.int32), "dest", (T, K))
+    _shape(_gpu(counts.is_in_rank, "is_in_rank", torch.uint8), "is_in_rank", (T, P))
+    _gpu(counts.send_counts, "send_counts", torch.int32)
+    if counts.send_counts.numel() != P:
+        raise ValueError("send_counts must hold P counts (one chunk)")
+    if counts.tokens_per_expert is not None:
+        _gpu(counts.tokens_per_expert, "tokens_per_expert", torch.int32)
+        if counts.tokens_per_expert.numel() != E:
+            raise ValueError("tokens_per_expert must hold E counts")
+    _shape(_gpu(counts.diag, "diag", torch.int32), "diag", (1,))
+    if out is None:
+        out = SendLayout(
+            send_token_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+            send_rank=torch.empty(cap, dtype=torch.int32, device=dev),
+            send_idx=torch.empty((cap, K), dtype=torch.int32, device=dev),
+            send_w=torch.empty((cap, K), dtype=torch.float32, device=dev),
+            token_row=torch.empty((T, K), dtype=torch.int32, device=dev))
+    for name, t, dt in (("send_token_idx", out.send_token_idx, torch.int32),
+                        ("send_rank", out.send_rank, torch.int32),
+                        ("send_idx", out.send_idx, torch.int32),
+                        ("send_w", out.send_w, torch.float32)):
+        _gpu(t, name, dt)
+        if t.shape[0] < cap:
+            raise ValueError(f"{name} holds fewer than {cap} rows")
+    if out.send_idx.dim() != 2 or out.send_idx.shape[1] != K or out.send_w.shape[1:] != (K,):
+        raise ValueError("send_idx / send_w must be [cap, K]")
+    _shape(_gpu(out.token_row, "token_row", torch.int32), "token_row", (T, K))
+    if workspace is None:
+        workspace = workspace_for(ep_dispatch_layout_workspace_bytes(T, P, El), dev, stream,
+                                  "fused")
+    _gpu(workspace, "workspace", torch.uint8)
+    st = lib().ep_dispatch_layout(
+        _vp(topk_idx), _vp(topk_weights), T, K, P, El, cap, _vp(counts.dest),
+        _vp(counts.is_in_rank), _vp(counts.send_counts), _vp(counts.tokens_per_expert),
+        _vp(counts.diag), _vp(out.send_token_idx), _vp(out.send_rank), _vp(out.send_idx),
+        _vp(out.send_w), _vp(out.token_row), _vp(workspace), workspace.numel(),
+        _stream(stream))
+    check(st, "ep_dispatch_layout")
+    return counts, out
 
 
 def ep_dispatch_permute(x: torch.Tensor, token_row: torch.Tensor, num_send_capacity: int, *,

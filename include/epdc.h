@@ -179,6 +179,52 @@ int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights,
                          hipStream_t stream);
 
 /*
+ * Bytes of workspace ep_dispatch_layout needs: a 256-byte header (uint32
+ * words: [0] barrier arrivals, [2] barrier generation, [3] error flags: bit 0
+ * = a barrier wait gave up) followed by one row of P + E + 1 uint32 per
+ * workgroup, min(ceil(T/256), 256) rows.  Zero-filled once before first use;
+ * every call leaves it ready for the next; calls that may overlap in time
+ * must use different workspaces.
+ */
+size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
+                                          int num_local_experts);
+
+/*
+ * Counts and send layout in one launch: the outputs of
+ * ep_compute_send_counts (one chunk) and of ep_build_send_layout, bit for
+ * bit the same, without the host seeing the counts in between.
+ * axolotl "torch_dispatch": compute_send_counts + build_send_layout (the
+ * module overview's send layout); NeMo "uccl_ep.buffer":
+ * Buffer.get_dispatch_layout.
+ *
+ *   topk_idx, topk_weights      [T,K] int64 / fp32 in
+ *   num_send_capacity           rows the send arrays hold; pairs past it are
+ *                               not written and their slots get token_row -1
+ *                               (T*min(K,P) always suffices)
+ *   dest, is_in_rank, send_counts [P], tokens_per_expert [E] (may be NULL),
+ *   diag (may be NULL)          as ep_compute_send_counts with C = 1
+ *   send_token_idx, send_rank, send_idx, send_w, token_row
+ *                               as ep_build_send_layout
+ *   workspace                   ep_dispatch_layout_workspace_bytes(T, P, E_local)
+ * The launch uses at most one workgroup per compute unit and one grid-wide
+ * barrier; the workgroups must be able to run at the same time, which holds
+ * unless other work keeps the device full for the barrier's whole time-out
+ * (about 0.1 s), after which the call gives up, sets the error bit in the
+ * workspace header and its outputs are undefined.  Returns
+ * EP_ERR_UNSUPPORTED when a workgroup's LDS share (P, E and the tiles per
+ * workgroup) would exceed 64 KiB; the two separate calls cover those sizes.
+ */
+int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights,
+                       int64_t num_tokens, int num_topk, int num_ranks,
+                       int num_local_experts, int64_t num_send_capacity,
+                       int32_t* dest, uint8_t* is_in_rank, int32_t* send_counts,
+                       int32_t* tokens_per_expert, int32_t* diag,
+                       int32_t* send_token_idx, int32_t* send_rank,
+                       int32_t* send_idx, float* send_w, int32_t* token_row,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
  * Row permute into the send buffer (optionally quantizing to fp8).
  * axolotl "torch_dispatch": dispatch (row n of the send buffer is hidden row
  * send_token_idx[n]); NeMo "uccl_ep.buffer": Buffer.dispatch /

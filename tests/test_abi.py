@@ -16,6 +16,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 EXPECTED = {
     "ep_abi_version", "ep_status_string", "ep_counts_workspace_bytes", "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
+    "ep_dispatch_layout_workspace_bytes", "ep_dispatch_layout",
     "ep_dispatch_permute", "ep_batched_prepare", "ep_combine",
 }
 
@@ -98,6 +99,33 @@ def test_layout_rejects_bad_workspace_and_capacity():
     assert call(ws=A8) == _lib.EP_ERR_WORKSPACE                # not 256-aligned
     assert call(cap=-1) == _lib.EP_ERR_INVALID_ARG
     assert call(cap=1 << 31) == _lib.EP_ERR_UNSUPPORTED
+
+
+def test_fused_layout_workspace_and_arguments():
+    L = _lib.lib()
+    # one row of P + E + 1 words per workgroup, min(tiles of 256, 256) rows
+    assert L.ep_dispatch_layout_workspace_bytes(16384, 32, 8) == 256 + 64 * (32 + 256 + 1) * 4
+    assert L.ep_dispatch_layout_workspace_bytes(0, 2, 4) == 256 + 1 * (2 + 8 + 1) * 4
+    assert L.ep_dispatch_layout_workspace_bytes(1 << 20, 8, 8) == 256 + 256 * (8 + 64 + 1) * 4
+    assert L.ep_dispatch_layout_workspace_bytes(-1, 2, 4) == 0
+    f = L.ep_dispatch_layout
+
+    def call(T=16, K=2, P=2, El=4, cap=64, dest=A16, ws=A16, ws_bytes=1 << 22, tpe=None):
+        return f(A16, A16, T, K, P, El, cap, dest, A16, A16, tpe, None, A16, A16, A16, A16,
+                 A16, ws, ws_bytes, None)
+    assert call(T=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(K=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(K=17) == _lib.EP_ERR_UNSUPPORTED
+    assert call(cap=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(cap=1 << 31) == _lib.EP_ERR_UNSUPPORTED
+    assert call(dest=None) == _lib.EP_ERR_INVALID_ARG
+    assert call(dest=ODD) == _lib.EP_ERR_INVALID_ARG
+    assert call(tpe=ODD) == _lib.EP_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.EP_ERR_WORKSPACE
+    assert call(ws=A8) == _lib.EP_ERR_WORKSPACE
+    assert call(ws_bytes=64) == _lib.EP_ERR_WORKSPACE
+    # LDS share over 64 KiB (1024 destinations x 8 experts): use the two calls
+    assert call(P=1024, El=8) == _lib.EP_ERR_UNSUPPORTED
 
 
 def test_permute_and_combine_reject_bad_rows():
