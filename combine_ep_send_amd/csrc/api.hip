@@ -235,6 +235,7 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
   a.send_w = send_w;
   a.token_row = token_row;
   a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
+  a.vec_in = (num_topk % 4) == 0 && aligned(topk_idx, 16) && aligned(topk_weights, 16);
   a.ctrl = static_cast<uint32_t*>(workspace);
   a.rows = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
   a.tiles = tiles;

@@ -89,6 +89,7 @@ struct FusedArgs {
   float* send_w;
   int32_t* token_row;
   bool vec_rows;                 // K % 4 == 0 and send_idx/send_w 16-byte aligned
+  bool vec_in;                   // K % 4 == 0 and topk_idx/topk_weights 16-byte aligned
   uint32_t* ctrl;                // workspace header: [0] arrivals, [2] barrier generation
   uint32_t* rows;                // [groups, P + E + 1] published totals
   int64_t tiles;                 // tiles of 256 tokens (>= 1)

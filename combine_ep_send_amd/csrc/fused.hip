@@ -40,20 +40,43 @@ template <int KMAX>
 __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid,
                                        TileSlots<KMAX>& s) {
   s.bad = 0;
+  if (valid && a.vec_in && a.K == KMAX) {
+    // whole rows of ids and weights as 16-byte loads
+    const u32x4* pi = reinterpret_cast<const u32x4*>(a.topk_idx + t * KMAX);
+    const u32x4* pw = reinterpret_cast<const u32x4*>(a.topk_weights + t * KMAX);
+#pragma unroll
+    for (int q = 0; q < KMAX / 2; ++q) {
+      const u32x4 v = pi[q];
+      s.ids[2 * q] = int64_t((uint64_t(v.y) << 32) | v.x);
+      s.ids[2 * q + 1] = int64_t((uint64_t(v.w) << 32) | v.z);
+    }
+#pragma unroll
+    for (int q = 0; q < KMAX / 4; ++q) {
+      const u32x4 v = pw[q];
+      s.wts[4 * q] = __uint_as_float(v.x);
+      s.wts[4 * q + 1] = __uint_as_float(v.y);
+      s.wts[4 * q + 2] = __uint_as_float(v.z);
+      s.wts[4 * q + 3] = __uint_as_float(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      s.ids[k] = -1;
+      s.wts[k] = 0.0f;
+      if (valid && k < a.K) {
+        s.ids[k] = a.topk_idx[t * a.K + k];
+        s.wts[k] = a.topk_weights[t * a.K + k];
+      }
+    }
+  }
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
+    const int64_t v = s.ids[k];
     s.bin[k] = -1;
-    s.ids[k] = -1;
-    s.wts[k] = 0.0f;
-    if (valid && k < a.K) {
-      const int64_t v = a.topk_idx[t * a.K + k];
-      s.ids[k] = v;
-      s.wts[k] = a.topk_weights[t * a.K + k];
-      if (v >= 0 && v < a.E)
-        s.bin[k] = int(v) / a.E_local;
-      else if (v != -1)
-        ++s.bad;
-    }
+    if (v >= 0 && v < a.E)
+      s.bin[k] = int(v) / a.E_local;
+    else if (v != -1)
+      ++s.bad;
   }
 }
 
@@ -87,7 +110,6 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   int32_t* s_hist = s_tcnt + a.tiles_per_group * P;                          // [nh]
   int32_t* s_tot = s_hist + nh;                                              // [P]
   int32_t* s_base = s_tot + P;                                               // [P]
-  __shared__ uint32_t s_gen;
   __shared__ int32_t s_bad;
 
   const int tid = threadIdx.x;
@@ -101,10 +123,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   const int my_tiles = tile1 > tile0 ? int(tile1 - tile0) : 0;
   const bool want_e = a.tokens_per_expert != nullptr;
 
-  if (tid == 0) {
-    s_gen = ld_relaxed(&a.ctrl[kCtrlEpoch]);
-    s_bad = 0;
-  }
+  // The barrier generation is read now and first used at the barrier, so
+  // its round trip overlaps the decode.
+  const uint32_t gen = tid == 0 ? ld_relaxed(&a.ctrl[kCtrlEpoch]) : 0u;
+  if (tid == 0) s_bad = 0;
   for (int i = tid; i < nh; i += kBlock) s_hist[i] = 0;
   __syncthreads();
 
@@ -158,7 +180,6 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   __builtin_amdgcn_s_waitcnt(0);   // this thread's row stores are performed
   __syncthreads();
   if (tid == 0) {
-    const uint32_t gen = s_gen;
     if (fetch_add_relaxed(&a.ctrl[kCtrlTicket], 1u) == uint32_t(G - 1)) {
       st_relaxed(&a.ctrl[kCtrlTicket], 0u);
       st_relaxed(&a.ctrl[kCtrlEpoch], gen + 1u);
@@ -176,62 +197,62 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   __syncthreads();
 
   // ---- 3. totals, bases, expert slice -----------------------------------------
-  for (int b = tid; b < P; b += kBlock) {
-    s_tot[b] = 0;
-    s_base[b] = 0;
-  }
-  __syncthreads();
-  const uint32_t* rows_in = a.rows;
-  {
-    // (group, destination) pairs, 8 loads in flight per thread
-    const int64_t n = int64_t(G) * P;
-    for (int64_t i0 = tid; i0 < n; i0 += int64_t(kBlock) * 8) {
-      uint32_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + int64_t(u) * kBlock;
-        v[u] = 0u;
-        if (i < n) v[u] = ld_relaxed(rows_in + (i / P) * nh + (i % P));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + int64_t(u) * kBlock;
-        if (i < n && v[u]) {
-          const int grp = int(i / P), b = int(i % P);
-          atomicAdd(&s_tot[b], int(v[u]));
-          if (grp < g) atomicAdd(&s_base[b], int(v[u]));
-        }
-      }
-    }
-  }
-  // experts [e0, e1) of this workgroup's slice, and the bad-id total (group 0)
+  // experts [e0, e1) are this workgroup's slice of the expert totals
   const int per_g = (a.E + G - 1) / G;
   const int e0 = g * per_g;
   const int e1 = min(a.E, e0 + per_g);
   const int ne = want_e && e1 > e0 ? e1 - e0 : 0;
-  int32_t* s_etot = s_hist;            // reuse: [ne] expert totals
+  int32_t* s_etot = s_hist;            // reuse (the row is published): [ne] expert totals
+  for (int b = tid; b < P; b += kBlock) {
+    s_tot[b] = 0;
+    s_base[b] = 0;
+  }
   for (int i = tid; i < ne; i += kBlock) s_etot[i] = 0;
   __syncthreads();
   {
-    const int64_t n = int64_t(G) * ne;
-    for (int64_t i0 = tid; i0 < n; i0 += int64_t(kBlock) * 8) {
-      uint32_t v[8];
+    // (group, destination) and (group, expert of the slice) pairs, all loads
+    // of a batch in flight together; groups start at different rows so the
+    // same words are not all requested at once.
+    const uint32_t* rows_in = a.rows;
+    const int nd = G * P;
+    const int nx = G * ne;
+    const int n = nd > nx ? nd : nx;
+    for (int i0 = tid; i0 < n; i0 += kBlock * 8) {
+      uint32_t vd[8], vx[8];
+      int gd[8], bd[8], ex[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + int64_t(u) * kBlock;
-        v[u] = 0u;
-        if (i < n) v[u] = ld_relaxed(rows_in + (i / ne) * nh + P + e0 + (i % ne));
+        const int i = i0 + u * kBlock;
+        vd[u] = 0u;
+        vx[u] = 0u;
+        gd[u] = 0;
+        bd[u] = 0;
+        ex[u] = 0;
+        if (i < nd) {
+          int grp = i / P + g;
+          if (grp >= G) grp -= G;
+          gd[u] = grp;
+          bd[u] = i % P;
+          vd[u] = ld_relaxed(rows_in + int64_t(grp) * nh + bd[u]);
+        }
+        if (i < nx) {
+          ex[u] = i % ne;
+          vx[u] = ld_relaxed(rows_in + int64_t(i / ne) * nh + P + e0 + ex[u]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + int64_t(u) * kBlock;
-        if (i < n && v[u]) atomicAdd(&s_etot[int(i % ne)], int(v[u]));
+        if (vd[u]) {
+          atomicAdd(&s_tot[bd[u]], int(vd[u]));
+          if (gd[u] < g) atomicAdd(&s_base[bd[u]], int(vd[u]));
+        }
+        if (vx[u]) atomicAdd(&s_etot[ex[u]], int(vx[u]));
       }
     }
   }
   if (g == 0 && a.diag) {
     for (int grp = tid; grp < G; grp += kBlock) {
-      const uint32_t v = ld_relaxed(rows_in + int64_t(grp) * nh + nh - 1);
+      const uint32_t v = ld_relaxed(a.rows + int64_t(grp) * nh + nh - 1);
       if (v) atomicAdd(&s_bad, int(v));
     }
   }
