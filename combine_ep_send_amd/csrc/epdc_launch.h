@@ -125,6 +125,8 @@ hipError_t launch_zero_pad(const PadArgs& a, hipStream_t s);
 
 // Largest workgroup of the combine (one 16-byte piece per thread).
 constexpr int kMaxRowBlock = 1024;
+// Workgroup of the bf16 permute (one 16-byte piece per thread).
+constexpr int kPermuteBlock = 128;
 
 struct CombineArgs {
   const void* y;

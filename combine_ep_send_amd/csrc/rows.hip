@@ -60,37 +60,40 @@ __device__ __forceinline__ int token_rows(const int32_t* token_row, int64_t t, i
 }
 
 // ---------------------------------------------------------------------------
-// bf16 permute, token-major: one wave per (token, chunk of 64*PER pieces);
-// the chunk of hidden row t is read once and stored to each of its rows.
-// Also fills the data rows of the expert-batched layout (token_row then
-// holds e*max + slot).
+// bf16 permute, token-major: one workgroup of kPermuteBlock threads per
+// (token, chunk of kPermuteBlock pieces), one 16-byte piece per thread; the
+// chunk of hidden row t is read once and stored to each of its rows.  Also
+// fills the data rows of the expert-batched layout (token_row then holds
+// e*max + slot).
 // ---------------------------------------------------------------------------
 template <int KMAX, int PER>
-__global__ __launch_bounds__(kWave) void permute_bf16_kernel(RowArgs a, int nchunks,
-                                                             int64_t item0) {
+__global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, int nchunks,
+                                                                     int64_t item0) {
   const int lane = threadIdx.x;
   const int H8 = a.H >> 3;
   const int64_t item = item0 + blockIdx.x;
   const int64_t t = udiv(item, nchunks);
-  const int j0 = int(item - t * nchunks) * (kWave * PER);
-  int32_t rows[KMAX];
-  bool use[KMAX];
-  if (token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use) == 0) return;
+  const int j0 = int(item - t * nchunks) * (kPermuteBlock * PER);
+  // The row is loaded before its destinations are known: both round trips
+  // overlap (a token with no destination wastes one load).
   const u32x4* src = static_cast<const u32x4*>(a.x) + t * H8;
-  u32x4* dst = static_cast<u32x4*>(a.out);
   u32x4 v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int j = j0 + i * kWave + lane;
+    const int j = j0 + i * kPermuteBlock + lane;
     if (j < H8) v[i] = ld_stream(src + j);
   }
+  int32_t rows[KMAX];
+  bool use[KMAX];
+  token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
+  u32x4* dst = static_cast<u32x4*>(a.out);
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     if (!use[k]) continue;
     u32x4* d = dst + int64_t(rows[k]) * H8;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int j = j0 + i * kWave + lane;
+      const int j = j0 + i * kPermuteBlock + lane;
       if (j < H8) st_stream(d + j, v[i]);
     }
   }
@@ -118,9 +121,8 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
   const int64_t item = item0 + blockIdx.x;
   const int64_t t = udiv(item, nchunks);
   const int p0 = int(item - t * nchunks) * (kWave * IT);
-  int32_t rows[KMAX];
-  bool use[KMAX];
-  if (token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use) == 0) return;
+  // The row is loaded before its destinations are known (as in the bf16
+  // permute), so both round trips overlap.
   const u32x4* src = static_cast<const u32x4*>(a.x) + t * H8;
   u32x4 in[IT][2];
 #pragma unroll
@@ -133,6 +135,9 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
       in[it][1] = ld_stream(src + 2 * p + 1);
     }
   }
+  int32_t rows[KMAX];
+  bool use[KMAX];
+  token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
   u32x4 q[IT];
   float sc[IT];
 #pragma unroll
@@ -286,28 +291,18 @@ inline Split split_row(int64_t units, int most) {
   return Split{int(n), int((per_lane + n - 1) / n)};
 }
 
-template <int KMAX, int PER>
-void launch_permute_bf16_p(const RowArgs& a, Split sp, hipStream_t s) {
-  for_each_launch(a.T * sp.nchunks, [&](int64_t i0, unsigned g) {
-    permute_bf16_kernel<KMAX, PER><<<g, kWave, 0, s>>>(a, sp.nchunks, i0);
-  });
-}
-
 template <int KMAX>
 void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
-  // Up to 2 pieces per lane: a 7168-channel row is seven chunks of 2 KiB.
-  // Short waves keep the scatter's stores streaming; larger chunks at full
-  // occupancy put so many rows in flight that the stores slow down.
-  const Split sp = split_row(a.H >> 3, 2);
-  switch (sp.per) {
-    case 1: launch_permute_bf16_p<KMAX, 1>(a, sp, s); break;
-    case 2: launch_permute_bf16_p<KMAX, 2>(a, sp, s); break;
-    case 3: launch_permute_bf16_p<KMAX, 3>(a, sp, s); break;
-    case 4: launch_permute_bf16_p<KMAX, 4>(a, sp, s); break;
-    case 5: launch_permute_bf16_p<KMAX, 5>(a, sp, s); break;
-    case 6: launch_permute_bf16_p<KMAX, 6>(a, sp, s); break;
-    default: launch_permute_bf16_p<KMAX, 7>(a, sp, s); break;
-  }
+  // One piece per thread, two waves per workgroup: a 7168-channel row is
+  // seven chunks of 2 KiB.  Of the shapes measured on the cache-cleared
+  // 16k-token scatter (1-7 pieces per lane, 1-4 waves per workgroup) this
+  // one moved the rows fastest: short-lived waves keep the stores streaming,
+  // while larger chunks at full occupancy put so many rows in flight that
+  // the stores slow down.
+  const int nchunks = int(((a.H >> 3) + kPermuteBlock - 1) / kPermuteBlock);
+  for_each_launch(a.T * nchunks, [&](int64_t i0, unsigned g) {
+    permute_bf16_kernel<KMAX, 1><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
+  });
 }
 
 template <int KMAX, int IT>
