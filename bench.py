@@ -309,12 +309,13 @@ def cpu_baseline(s, budget_tokens):
     }
 
 
-KERNEL_SOURCES = ("rows.hip", "epdc_device.h", "epdc_launch.h")
+KERNEL_SOURCES = ("scan.hip", "fused.hip", "rows.hip", "api.hip", "epdc_device.h",
+                  "epdc_launch.h")
 
 
 def kernel_source_digest():
-    """SHA-256 over the sources of the row kernels (the measured traffic is
-    only valid for the code it was measured on)."""
+    """SHA-256 over the library's sources (the measured traffic is only
+    valid for the code it was measured on)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "combine_ep_send_amd", "csrc", name), "rb") as f:

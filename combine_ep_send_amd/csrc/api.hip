@@ -323,6 +323,7 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_token
   r.capacity = int64_t(num_local_experts) * max_num_tokens;
   r.out = b_x;
   r.out_scale = nullptr;
+  r.sparse = true;
   return launch_status(launch_permute_bf16(r, stream));
 }
 

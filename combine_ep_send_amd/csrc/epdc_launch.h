@@ -110,6 +110,7 @@ struct RowArgs {
   int64_t capacity;              // rows of the destination buffer
   void* out;
   float* out_scale;              // fp8 scales or null
+  bool sparse;                   // many tokens have no destination: look up rows first
 };
 hipError_t launch_permute_bf16(const RowArgs& a, hipStream_t s);
 hipError_t launch_permute_fp8(const RowArgs& a, hipStream_t s);

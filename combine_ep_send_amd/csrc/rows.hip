@@ -66,7 +66,7 @@ __device__ __forceinline__ int token_rows(const int32_t* token_row, int64_t t, i
 // fills the data rows of the expert-batched layout (token_row then holds
 // e*max + slot).
 // ---------------------------------------------------------------------------
-template <int KMAX, int PER>
+template <int KMAX, int PER, bool LOAD_FIRST>
 __global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, int nchunks,
                                                                      int64_t item0) {
   const int lane = threadIdx.x;
@@ -74,18 +74,20 @@ __global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, 
   const int64_t item = item0 + blockIdx.x;
   const int64_t t = udiv(item, nchunks);
   const int j0 = int(item - t * nchunks) * (kPermuteBlock * PER);
-  // The row is loaded before its destinations are known: both round trips
-  // overlap (a token with no destination wastes one load).
+  // LOAD_FIRST: the row is loaded before its destinations are known, so both
+  // round trips overlap; a token with no destination then wastes one load,
+  // which is why the sparse expert-batched fill looks up the rows first.
   const u32x4* src = static_cast<const u32x4*>(a.x) + t * H8;
   u32x4 v[PER];
+  int32_t rows[KMAX];
+  bool use[KMAX];
+  if (!LOAD_FIRST && token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use) == 0) return;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = j0 + i * kPermuteBlock + lane;
     if (j < H8) v[i] = ld_stream(src + j);
   }
-  int32_t rows[KMAX];
-  bool use[KMAX];
-  token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
+  if (LOAD_FIRST) token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
   u32x4* dst = static_cast<u32x4*>(a.out);
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
@@ -301,7 +303,10 @@ void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
   // the stores slow down.
   const int nchunks = int(((a.H >> 3) + kPermuteBlock - 1) / kPermuteBlock);
   for_each_launch(a.T * nchunks, [&](int64_t i0, unsigned g) {
-    permute_bf16_kernel<KMAX, 1><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
+    if (a.sparse)
+      permute_bf16_kernel<KMAX, 1, false><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
+    else
+      permute_bf16_kernel<KMAX, 1, true><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
   });
 }
 
