@@ -7,8 +7,8 @@ A step is one pass of the whole hot path over one batch of seeded synthetic
 routing, with inputs already resident in HBM:
   send layouts:  counts + send layout (one launch) -> row permute -> combine
   batched:       batched prepare (zero-padded) -> combine
-  fp8 chunked:   counts (all chunks) -> per chunk, alternating 2 streams:
-                 send layout -> fp8 quantize-permute -> combine
+  fp8 chunked:   counts (all chunks), the chunks' send layouts, then per
+                 chunk, alternating 2 streams: fp8 quantize-permute -> combine
 The identity expert sits between dispatch and combine: combine reads the send
 rows themselves (bf16), or the dequantized fp8 rows prepared before timing.
 
@@ -181,12 +181,17 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     dev = d_x.device
     bounds = ep.chunk_bounds(T, C)
     streams = [torch.cuda.Stream(device=dev) for _ in range(s.streams)]
+    # Chunk i's permute and combine run on stream i mod S.  The layouts are
+    # latency-bound: chunk 0's runs first on stream 0, the later chunks' run
+    # back to back on stream 1 while chunk 0's permute streams rows.
+    work_st = [streams[i % len(streams)] for i in range(C)]
+    lay_st = [streams[0] if i == 0 or len(streams) == 1 else streams[1] for i in range(C)]
     counts = ep.ep_compute_send_counts(d_idx, P, El, C, expert_counts=False)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     per = []
     for i, (a, b) in enumerate(bounds):
-        st = streams[i % len(streams)]
+        st = lay_st[i]
         cap = (b - a) * min(K, P)
         ws = ep.workspace_for(ep.ep_layout_workspace_bytes(b - a, P), dev, st)
         with torch.cuda.stream(st):
@@ -194,7 +199,7 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
                                           counts.send_counts[i], P, El, cap, stream=st,
                                           workspace=ws)
             q, sc = ep.ep_dispatch_permute(d_x[a:b], lay.token_row, cap, fp8=True, stream=st)
-        per.append(dict(a=a, b=b, st=st, cap=cap, lay=lay, q=q, sc=sc, ws=ws))
+        per.append(dict(a=a, b=b, cap=cap, lay=lay, q=q, sc=sc, ws=ws))
     torch.cuda.synchronize()
     # identity expert behind fp8: y = bf16(decode(q) * scale), built once
     for c in per:
@@ -204,17 +209,21 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     main = torch.cuda.current_stream()
 
     def step(timer=None):
+        s0 = streams[0]
         start = torch.cuda.Event()
         start.record(main)
-        tk = timer.start("counts", main) if timer else None
-        ep.ep_compute_send_counts(d_idx, P, El, C, expert_counts=False, out=counts)
+        s0.wait_event(start)
+        tk = timer.start("counts", s0) if timer else None
+        ep.ep_compute_send_counts(d_idx, P, El, C, expert_counts=False, out=counts, stream=s0)
         if timer:
             timer.stop(tk)
         ready = torch.cuda.Event()
-        ready.record(main)
-        for i, c in enumerate(per):
-            st = c["st"]
+        ready.record(s0)
+        for st in streams[1:]:
             st.wait_event(ready)
+        laid = []
+        for i, c in enumerate(per):
+            st = lay_st[i]
             a, b = c["a"], c["b"]
             tk = timer.start("layout", st) if timer else None
             ep.ep_build_send_layout(d_idx[a:b], d_w[a:b], counts.dest[a:b],
@@ -222,7 +231,15 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
                                     workspace=c["ws"], stream=st)
             if timer:
                 timer.stop(tk)
-                tk = timer.start("permute_fp8", st)
+            ev = torch.cuda.Event()
+            ev.record(st)
+            laid.append(ev)
+        for i, c in enumerate(per):
+            st = work_st[i]
+            if st is not lay_st[i]:
+                st.wait_event(laid[i])
+            a, b = c["a"], c["b"]
+            tk = timer.start("permute_fp8", st) if timer else None
             ep.ep_dispatch_permute(d_x[a:b], c["lay"].token_row, c["cap"], fp8=True, out=c["q"],
                                    out_scale=c["sc"], stream=st)
             if timer:

@@ -131,8 +131,10 @@ def dispatch_chunked_forward(x: torch.Tensor, topk_idx: torch.Tensor, topk_weigh
     reach the host in one copy and size each chunk's buffers, otherwise each
     chunk gets the worst case T_c * min(K, P) rows.  ``local_kernel(recv_x,
     recv_idx, recv_w)`` returns the bf16 expert output [rows, H]; it runs on
-    the chunk's stream.  Chunk c+1's dispatch is enqueued before chunk c's
-    combine result is needed, so the streams overlap."""
+    the chunk's stream.  Every chunk's layout is enqueued before chunk 0's
+    expert kernel, and chunk c+1's permute before chunk c's combine result is
+    needed, so the streams overlap; the latency-bound layouts of chunks >= 1
+    run on the second stream while chunk 0's rows stream on the first."""
     T, K = topk_idx.shape
     H = x.shape[1]
     P = int(num_ranks)
@@ -141,26 +143,44 @@ def dispatch_chunked_forward(x: torch.Tensor, topk_idx: torch.Tensor, topk_weigh
     if streams is None:
         streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
     bounds = chunk_bounds(T, chunks)
-    c = ep_compute_send_counts(topk_idx, P, num_local_experts, chunks, expert_counts=False)
+    s0 = streams[0]
+    s0.wait_stream(main)
+    c = ep_compute_send_counts(topk_idx, P, num_local_experts, chunks, expert_counts=False,
+                               stream=s0)
     if exact_counts:
-        caps = [int(v) for v in to_host(c.send_counts).sum(dim=1)]
+        with torch.cuda.stream(s0):
+            caps = [int(v) for v in to_host(c.send_counts).sum(dim=1)]
     else:
         caps = [(e - s) * min(K, P) for s, e in bounds]
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ready = torch.cuda.Event()
-    ready.record(main)
-    for i, (s, e) in enumerate(bounds):
-        st = streams[i % len(streams)]
+    ready.record(s0)
+    for st in streams[1:]:
         st.wait_event(ready)
+    # Layouts: chunk 0's on stream 0, the later chunks' back to back on
+    # stream 1 while chunk 0's permute runs (they are latency-bound).
+    lays, laid = [], []
+    for i, (s, e) in enumerate(bounds):
+        st = s0 if i == 0 or len(streams) == 1 else streams[1]
+        lay = None
+        if e > s:
+            lay = ep_build_send_layout(topk_idx[s:e], topk_weights[s:e], c.dest[s:e],
+                                       c.send_counts[i], P, num_local_experts, caps[i],
+                                       stream=st)
+        ev = torch.cuda.Event()
+        ev.record(st)
+        lays.append(lay)
+        laid.append(ev)
+    for i, (s, e) in enumerate(bounds):
+        if e == s:
+            continue
+        st = streams[i % len(streams)]
+        st.wait_event(laid[i])
         with torch.cuda.stream(st):
-            if e == s:
-                continue
-            idx_c, w_c = topk_idx[s:e], topk_weights[s:e]
-            lay = ep_build_send_layout(idx_c, w_c, c.dest[s:e], c.send_counts[i], P,
-                                       num_local_experts, caps[i], stream=st)
+            lay = lays[i]
             recv_x = ep_dispatch_permute(x[s:e], lay.token_row, caps[i], fp8=fp8, stream=st)
             y = local_kernel(recv_x, lay.send_idx, lay.send_w)
-            ep_combine(y, lay.token_row, w_c, out=out[s:e], stream=st)
+            ep_combine(y, lay.token_row, topk_weights[s:e], out=out[s:e], stream=st)
     for st in streams:
         done = torch.cuda.Event()
         done.record(st)
