@@ -319,13 +319,10 @@ void launch_permute_fp8_p(const RowArgs& a, Split sp, hipStream_t s) {
 
 template <int KMAX>
 void launch_permute_fp8_k(const RowArgs& a, hipStream_t s) {
-  const Split sp = split_row(a.H >> 4, 4);
-  switch (sp.per) {
-    case 1: launch_permute_fp8_p<KMAX, 1>(a, sp, s); break;
-    case 2: launch_permute_fp8_p<KMAX, 2>(a, sp, s); break;
-    case 3: launch_permute_fp8_p<KMAX, 3>(a, sp, s); break;
-    default: launch_permute_fp8_p<KMAX, 4>(a, sp, s); break;
-  }
+  // One 16-channel piece per lane, one wave per 1024 channels (7 per 7168-
+  // channel row): the fastest of the shapes measured (1-7 pieces per lane,
+  // 1-7 waves per workgroup) on the cache-cleared 8k-token chunk.
+  launch_permute_fp8_p<KMAX, 1>(a, split_row(a.H >> 4, 1), s);
 }
 
 template <int KMAX>
