@@ -58,6 +58,7 @@ __all__ = [
     "dispatch_permute_fp8",
     "batched_prepare",
     "combine",
+    "combine_partials",
     "FP8_MAX",
     "FP8_GROUP",
 ]
@@ -324,7 +325,17 @@ def batched_prepare(x_bits, topk_idx, first_expert, num_local_experts,
 # Combine
 # --------------------------------------------------------------------------
 
-def combine(y_bits, token_row, topk_weights):
+def _add_biases(acc, biases):
+    """[uccl] Buffer.combine ``bias``: one [T,H] tensor or a pair, added to
+    the reduced tokens.  Reading: each bias (bf16) is added to the float32
+    sum after the expert terms, in the order given, before the one rounding
+    to bf16."""
+    for b in biases:
+        acc = (acc + bf16_to_f32(np.asarray(b, dtype=np.uint16))).astype(np.float32)
+    return acc
+
+
+def combine(y_bits, token_row, topk_weights, biases=()):
     """[axolotl] combine, [uccl] Buffer.combine / low_latency_combine,
     [vllm] BatchedPrepareAndFinalize.finalize: the weighted per-token sum of
     expert outputs back onto the source tokens.
@@ -332,7 +343,8 @@ def combine(y_bits, token_row, topk_weights):
     out[t] = bf16( sum over k = 0..K-1 with r = token_row[t,k] >= 0 of
     w[t,k] * y[r] ), accumulated in float32 ([nemo] moe_router_dtype): each
     product is rounded to float32, then added to the running float32 sum
-    (which starts at +0.0) in ascending k.  Tokens with no routed slot give 0.
+    (which starts at +0.0) in ascending k.  Tokens with no routed slot give 0
+    (plus the biases, if any).
     """
     y = np.asarray(y_bits, dtype=np.uint16)
     row = np.asarray(token_row, dtype=np.int64)
@@ -347,4 +359,31 @@ def combine(y_bits, token_row, topk_weights):
             continue
         prod = (w[m, k][:, None] * bf16_to_f32(y[r[m]])).astype(np.float32)
         acc[m] = (acc[m] + prod).astype(np.float32)
-    return f32_to_bf16(acc)
+    return f32_to_bf16(_add_biases(acc, biases))
+
+
+def combine_partials(y_bits, token_row, biases=()):
+    """[axolotl] module overview and combine: the local expert kernel already
+    weights and sums over its slots, and combine sums the per-destination
+    partial outputs back onto the source tokens, without weights ([uccl]
+    Buffer.combine without topk_weights: "addition without weights").
+
+    Each distinct row of token t (the send row of one destination; slots
+    owned by the same destination share it) is added once, in the order of
+    its first slot (k ascending), to a float32 sum that starts at +0.0; then
+    the biases; then one rounding to bf16.
+    """
+    y = np.asarray(y_bits, dtype=np.uint16)
+    row = np.asarray(token_row, dtype=np.int64)
+    T, K = row.shape
+    H = y.shape[1]
+    acc = np.zeros((T, H), dtype=np.float32)
+    for t in range(T):
+        seen = []
+        for k in range(K):
+            r = int(row[t, k])
+            if r < 0 or r in seen:
+                continue
+            seen.append(r)
+            acc[t] = (acc[t] + bf16_to_f32(y[r])).astype(np.float32)
+    return f32_to_bf16(_add_biases(acc, biases))

@@ -47,6 +47,12 @@ ROUTING_PINS = [
     pin(RT, "test_layout_invariants_skewed"),
     pin(RT, "test_chunk_bounds_cases", GOLDEN),
 ]
+PARTIAL_PINS = [
+    pin(NUM, "test_combine_partials_counts_each_destination_once"),
+    pin(NUM, "test_combine_partials_within_1ulp_of_exact_sum"),
+    pin(NUM, "test_combine_partials_single_destination_is_copy"),
+    pin(NUM, "test_combine_biases_are_added"),
+]
 COMBINE_PINS = [
     pin(NUM, "test_combine_hand_worked", GOLDEN),
     pin(NUM, "test_combine_order_is_k_ascending"),
@@ -121,6 +127,21 @@ MUTANTS = {
     "fp8_zero_group_sign": (
         "q = np.where((scale > 0)[:, :, None], q, np.uint8(0))",
         "q = np.where((scale > 0)[:, :, None], q, np.uint8(0x80))", FORMAT_PINS),
+    "partials_duplicates_counted": (
+        "            if r < 0 or r in seen:",
+        "            if r < 0:", PARTIAL_PINS),
+    "partials_weighted_by_accident": (
+        "            acc[t] = (acc[t] + bf16_to_f32(y[r])).astype(np.float32)",
+        "            acc[t] = (acc[t] + 0.5 * bf16_to_f32(y[r])).astype(np.float32)",
+        PARTIAL_PINS),
+    "bias_dropped": (
+        "    for b in biases:\n        acc = (acc + bf16_to_f32(np.asarray(b, dtype=np.uint16)))",
+        "    for b in biases[:0]:\n        acc = (acc + bf16_to_f32(np.asarray(b, dtype=np.uint16)))",
+        PARTIAL_PINS),
+    "bias_subtracted": (
+        "acc = (acc + bf16_to_f32(np.asarray(b, dtype=np.uint16))).astype(np.float32)",
+        "acc = (acc - bf16_to_f32(np.asarray(b, dtype=np.uint16))).astype(np.float32)",
+        PARTIAL_PINS),
     "batched_slots_descending": (
         "tokens = np.flatnonzero(hit_slots.any(axis=1))",
         "tokens = np.flatnonzero(hit_slots.any(axis=1))[::-1]", BATCHED_PINS),
@@ -149,6 +170,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 def test_unmutated_copy_passes_all_pins(monkeypatch):
     mod = make_mutant("FP8_GROUP = 128", "FP8_GROUP = 128")
-    for module, fn, args in ROUTING_PINS + COMBINE_PINS + FORMAT_PINS + BATCHED_PINS:
+    for module, fn, args in (ROUTING_PINS + COMBINE_PINS + FORMAT_PINS + BATCHED_PINS +
+                             PARTIAL_PINS):
         monkeypatch.setattr(module, "O", mod)
         getattr(module, fn)(*args)

@@ -258,3 +258,60 @@ def test_combine_hand_worked(golden):
     outb = O.bf16_to_f32(O.combine(bx.reshape(-1, 8), btr, w))
     want = np.float32(b["combine_identity_scale"])[:, None] * O.bf16_to_f32(x)
     assert np.array_equal(outb, want)
+
+
+# --------------------------------------------------------------------------
+# unweighted per-destination partial sums, and combine biases
+# --------------------------------------------------------------------------
+
+def test_combine_partials_counts_each_destination_once():
+    # slots 0 and 1 share destination row 3, slot 2 is row 5: the partial of
+    # row 3 is added once, not twice (each destination sends one partial)
+    y = torch_bf16_bits(np.float32([[0.0], [0.0], [0.0], [1.5], [0.0], [0.25]]))
+    row = np.array([[3, 3, 5], [3, -1, 3], [-1, -1, -1]], dtype=np.int32)
+    out = O.bf16_to_f32(O.combine_partials(y, row))
+    assert out[:, 0].tolist() == [1.75, 1.5, 0.0]
+
+
+def test_combine_partials_within_1ulp_of_exact_sum():
+    rng = np.random.default_rng(6)
+    T, K, H, R = 200, 8, 32, 64
+    y = torch_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    row = rng.integers(-1, R, size=(T, K)).astype(np.int32)
+    out = O.bf16_to_f32(O.combine_partials(y, row)).astype(np.float64)
+    yf = O.bf16_to_f32(y).astype(np.float64)
+    exact = np.zeros((T, H))
+    mag = np.zeros((T, H))
+    for t in range(T):
+        for r in set(int(v) for v in row[t] if v >= 0):      # a set: distinct rows
+            exact[t] += yf[r]
+            mag[t] += np.abs(yf[r])
+    assert np.all(np.abs(out - exact) <= bf16_ulp(exact) + K * 2.0 ** -23 * mag)
+
+
+def test_combine_partials_single_destination_is_copy():
+    s = spec("tiny", T=300, H=64, P=1, E=8, K=2)
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, 1, 8)
+    out = O.combine_partials(O.dispatch_permute(x, sti), trow)
+    # one destination: every routed token's only row is its own hidden row
+    # (values compare equal; -0.0 comes back +0.0 since the sum starts at +0.0)
+    assert np.array_equal(O.bf16_to_f32(out), O.bf16_to_f32(x))
+
+
+def test_combine_biases_are_added():
+    # small integers: every sum is exact, so the result is the plain sum
+    y = torch_bf16_bits(np.float32([[1.0, 2.0], [4.0, 8.0]]))
+    row = np.array([[0, 1], [-1, -1]], dtype=np.int32)
+    w = np.float32([[1.0, 2.0], [0.0, 0.0]])
+    b0 = torch_bf16_bits(np.float32([[16.0, -32.0], [3.0, 5.0]]))
+    b1 = torch_bf16_bits(np.float32([[64.0, 1.0], [-7.0, 0.5]]))
+    got = O.bf16_to_f32(O.combine(y, row, w, biases=(b0,)))
+    assert got.tolist() == [[1 + 8 + 16, 2 + 16 - 32], [3, 5]]
+    got = O.bf16_to_f32(O.combine(y, row, w, biases=(b0, b1)))
+    assert got.tolist() == [[1 + 8 + 16 + 64, 2 + 16 - 32 + 1], [-4, 5.5]]
+    got = O.bf16_to_f32(O.combine_partials(y, row, biases=(b0, b1)))
+    assert got.tolist() == [[1 + 4 + 16 + 64, 2 + 8 - 32 + 1], [-4, 5.5]]
+    # a token with no slot returns the bias bit for bit
+    assert np.array_equal(O.combine(y, row, w, biases=(b0,))[1], b0[1])
