@@ -40,7 +40,7 @@ _SIGNATURES = {
     "ep_dispatch_permute": (_I32, [_P, _I64, _I32, _P, _I32, _I64, _I32, _P, _P, _P]),
     "ep_batched_prepare": (
         _I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
-    "ep_combine": (_I32, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "ep_combine": (_I32, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _P, _P]),
 }
 
 _lib = None

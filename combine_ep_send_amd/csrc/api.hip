@@ -328,20 +328,23 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_token
 }
 
 int ep_combine(const void* y, int64_t num_rows, const int32_t* token_row,
-               const float* topk_weights, int64_t num_tokens, int num_topk, int hidden, void* out,
-               hipStream_t stream) {
+               const float* topk_weights, int64_t num_tokens, int num_topk, int hidden,
+               const void* bias0, const void* bias1, void* out, hipStream_t stream) {
   if (num_tokens < 0 || num_topk < 1 || num_rows < 0) return EP_ERR_INVALID_ARG;
   if (num_tokens >= kMaxTokens || num_topk > EPDC_MAX_TOPK) return EP_ERR_UNSUPPORTED;
   int st = check_hidden(hidden, false);
   if (st != EP_OK) return st;
   if (!arr_ok(y, num_rows, 16) || !arr_ok(token_row, num_tokens, 4) ||
-      !arr_ok(topk_weights, num_tokens, 4) || !arr_ok(out, num_tokens, 16))
+      (topk_weights && !aligned(topk_weights, 4)) || !arr_ok(out, num_tokens, 16) ||
+      (bias0 && !aligned(bias0, 16)) || (bias1 && !aligned(bias1, 16)))
     return EP_ERR_INVALID_ARG;
   CombineArgs a{};
   a.y = y;
   a.R = num_rows;
   a.token_row = token_row;
   a.w = topk_weights;
+  a.bias0 = bias0;
+  a.bias1 = bias1;
   a.T = num_tokens;
   a.K = num_topk;
   a.H = hidden;

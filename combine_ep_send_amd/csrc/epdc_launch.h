@@ -133,7 +133,9 @@ struct CombineArgs {
   const void* y;
   int64_t R;
   const int32_t* token_row;
-  const float* w;
+  const float* w;                // null: unweighted, each distinct row once
+  const void* bias0;             // [T,H] bf16 or null
+  const void* bias1;             // [T,H] bf16 or null
   int64_t T;
   int K;
   int H;

@@ -203,13 +203,26 @@ __global__ __launch_bounds__(kBlock) void zero_pad_kernel(PadArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine: out[t] = bf16( sum_k w[t,k] * y[token_row[t,k]] ), fp32 product
-// rounded, then added in ascending k (no contraction into FMA).  One
-// workgroup per (token, chunk of blockDim.x pieces), one 16-byte piece per
-// thread: all distinct rows' loads are issued before the first add, and a
-// slot that repeats an earlier slot's row reuses its registers.
+// Combine.  Weighted: out[t] = bf16( sum_k w[t,k] * y[token_row[t,k]] ), the
+// fp32 product rounded, then added in ascending k (no contraction into FMA).
+// Unweighted (no weights given): each distinct row of t, i.e. each
+// destination's partial output, is added once, in the order of its first
+// slot.  Then up to two bias rows [T,H] are added, and the sum is rounded
+// once to bf16.  One workgroup per (token, chunk of blockDim.x pieces), one
+// 16-byte piece per thread: all distinct rows' loads are issued before the
+// first add, and a slot that repeats an earlier slot's row reuses its
+// registers.
 // ---------------------------------------------------------------------------
-template <int KMAX>
+__device__ __forceinline__ void add_row(float (&acc)[8], const u32x4& v) {
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] = acc[2 * q] + bf16_lo(wd[q]);
+    acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(wd[q]);
+  }
+}
+
+template <int KMAX, bool WEIGHTED>
 __global__ __launch_bounds__(kMaxRowBlock) void combine_kernel(CombineArgs a, int nchunks,
                                                                int64_t item0) {
 #pragma clang fp contract(off)
@@ -220,7 +233,7 @@ __global__ __launch_bounds__(kMaxRowBlock) void combine_kernel(CombineArgs a, in
   int32_t rows[KMAX];
   float wk[KMAX];
   load_slots<KMAX>(a.token_row, t, a.K, rows);
-  load_slots<KMAX>(a.w, t, a.K, wk);
+  if (WEIGHTED) load_slots<KMAX>(a.w, t, a.K, wk);
   bool use[KMAX];    // slot contributes
   int from[KMAX];    // slot whose loaded row it reuses (itself if first)
 #pragma unroll
@@ -239,11 +252,16 @@ __global__ __launch_bounds__(kMaxRowBlock) void combine_kernel(CombineArgs a, in
     v[k] = u32x4{0u, 0u, 0u, 0u};
     if (use[k] && from[k] == k) v[k] = ld_stream(y + int64_t(rows[k]) * H8 + j);
   }
+  u32x4 b0 = u32x4{0u, 0u, 0u, 0u}, b1 = u32x4{0u, 0u, 0u, 0u};
+  if (a.bias0) b0 = ld_stream(static_cast<const u32x4*>(a.bias0) + t * H8 + j);
+  if (a.bias1) b1 = ld_stream(static_cast<const u32x4*>(a.bias1) + t * H8 + j);
+  if (WEIGHTED) {
 #pragma unroll
-  for (int k = 1; k < KMAX; ++k) {
+    for (int k = 1; k < KMAX; ++k) {
 #pragma unroll
-    for (int q = 0; q < k; ++q)
-      if (from[k] == q) v[k] = v[q];
+      for (int q = 0; q < k; ++q)
+        if (from[k] == q) v[k] = v[q];
+    }
   }
   float acc[8];
 #pragma unroll
@@ -251,16 +269,22 @@ __global__ __launch_bounds__(kMaxRowBlock) void combine_kernel(CombineArgs a, in
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     if (!use[k]) continue;
-    const float wt = wk[k];
-    const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    if (WEIGHTED) {
+      const float wt = wk[k];
+      const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float p0 = wt * bf16_lo(wd[q]);
-      const float p1 = wt * bf16_hi(wd[q]);
-      acc[2 * q] = acc[2 * q] + p0;
-      acc[2 * q + 1] = acc[2 * q + 1] + p1;
+      for (int q = 0; q < 4; ++q) {
+        const float p0 = wt * bf16_lo(wd[q]);
+        const float p1 = wt * bf16_hi(wd[q]);
+        acc[2 * q] = acc[2 * q] + p0;
+        acc[2 * q + 1] = acc[2 * q + 1] + p1;
+      }
+    } else if (from[k] == k) {
+      add_row(acc, v[k]);
     }
   }
+  if (a.bias0) add_row(acc, b0);
+  if (a.bias1) add_row(acc, b1);
   u32x4 o;
   o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
   o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
@@ -334,7 +358,10 @@ void launch_combine_k(const CombineArgs& a, hipStream_t s) {
   const int64_t per_chunk = (H8 + nch - 1) / nch;
   const int threads = int((per_chunk + kWave - 1) / kWave) * kWave;
   for_each_launch(a.T * nch, [&](int64_t i0, unsigned g) {
-    combine_kernel<KMAX><<<g, threads, 0, s>>>(a, int(nch), i0);
+    if (a.w)
+      combine_kernel<KMAX, true><<<g, threads, 0, s>>>(a, int(nch), i0);
+    else
+      combine_kernel<KMAX, false><<<g, threads, 0, s>>>(a, int(nch), i0);
   });
 }
 

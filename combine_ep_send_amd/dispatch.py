@@ -114,10 +114,16 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor
 
 
 def combine(local_out: torch.Tensor, handle: DispatchHandle,
-            out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Weighted per-token sum of the expert outputs [N,H] back onto the
-    source tokens (axolotl combine; Buffer.combine with top-k weights)."""
-    return ep_combine(local_out, handle.token_row, handle.topk_weights, out=out)
+            out: Optional[torch.Tensor] = None, *, weighted: bool = True,
+            bias=None) -> torch.Tensor:
+    """Per-token sum of the expert outputs [N,H] back onto the source tokens.
+    ``weighted``: each slot's row times its top-k weight (Buffer.combine with
+    topk_weights).  Otherwise the local kernel has already weighted and
+    summed over its slots, and each destination's partial row is added once
+    (axolotl combine).  ``bias``: a [T,H] bf16 tensor or a pair, added
+    before the one rounding to bf16 (Buffer.combine bias)."""
+    return ep_combine(local_out, handle.token_row, handle.topk_weights if weighted else None,
+                      bias=bias, out=out)
 
 
 def dispatch_chunked_forward(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor,

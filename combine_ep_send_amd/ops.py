@@ -336,11 +336,15 @@ def ep_batched_prepare(x: torch.Tensor, topk_idx: torch.Tensor, first_expert: in
     return out, tokens_per_expert, token_row
 
 
-def ep_combine(y: torch.Tensor, token_row: torch.Tensor, topk_weights: torch.Tensor, *,
+def ep_combine(y: torch.Tensor, token_row: torch.Tensor,
+               topk_weights: Optional[torch.Tensor], *, bias=None,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """out [T, H] bf16 = weighted fp32 sum over k of y[token_row[t, k]].
-    ``y`` is [R, H] or any contiguous bf16 tensor whose last dim is H (e.g.
-    the batched buffer [E_local, max, H], read as E_local*max rows)."""
+    """out [T, H] bf16 = fp32 sum over k of w[t, k] * y[token_row[t, k]], or
+    with ``topk_weights=None`` the sum of each distinct row of t once (the
+    per-destination partial outputs), plus ``bias`` (a [T, H] bf16 tensor or
+    a pair of them).  ``y`` is [R, H] or any contiguous bf16 tensor whose last
+    dim is H (e.g. the batched buffer [E_local, max, H], read as E_local*max
+    rows)."""
     _gpu(y, "y", torch.bfloat16)
     if y.dim() < 2:
         raise ValueError("y must be [rows, H]")
@@ -348,11 +352,19 @@ def ep_combine(y: torch.Tensor, token_row: torch.Tensor, topk_weights: torch.Ten
     R = y.numel() // H if H else 0
     _gpu(token_row, "token_row", torch.int32, 2)
     T, K = token_row.shape
-    _shape(_gpu(topk_weights, "topk_weights", torch.float32), "topk_weights", (T, K))
+    if topk_weights is not None:
+        _shape(_gpu(topk_weights, "topk_weights", torch.float32), "topk_weights", (T, K))
+    biases = () if bias is None else (tuple(bias) if isinstance(bias, (tuple, list)) else (bias,))
+    if len(biases) > 2:
+        raise ValueError("bias is one [T, H] tensor or a pair")
+    for i, b in enumerate(biases):
+        _shape(_gpu(b, f"bias[{i}]", torch.bfloat16), f"bias[{i}]", (T, H))
+    b0 = biases[0] if len(biases) > 0 else None
+    b1 = biases[1] if len(biases) > 1 else None
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     _shape(_gpu(out, "out", torch.bfloat16), "out", (T, H))
-    st = lib().ep_combine(_vp(y), R, _vp(token_row), _vp(topk_weights), T, K, H, _vp(out),
-                          _stream(stream))
+    st = lib().ep_combine(_vp(y), R, _vp(token_row), _vp(topk_weights), T, K, H, _vp(b0),
+                          _vp(b1), _vp(out), _stream(stream))
     check(st, "ep_combine")
     return out

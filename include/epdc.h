@@ -72,7 +72,7 @@ typedef enum {
     EP_DTYPE_FP8_E4M3 = 1      /* OCP e4m3 (float8_e4m3fn) + fp32 scales */
 } ep_dtype_t;
 
-#define EPDC_ABI_VERSION 1
+#define EPDC_ABI_VERSION 2
 #define EPDC_MAX_TOPK 16
 #define EPDC_MAX_BINS 1024
 #define EPDC_FP8_GROUP 128
@@ -279,27 +279,36 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx,
                        hipStream_t stream);
 
 /*
- * Weighted combine back onto the source tokens.
- * axolotl "torch_dispatch": combine; NeMo "uccl_ep.buffer": Buffer.combine /
- * low_latency_combine (reduce with the top-k weights); vLLM
+ * Combine back onto the source tokens, weighted or as per-destination
+ * partial sums, with optional biases.
+ * axolotl "torch_dispatch": module overview and combine (the local kernel
+ * weights and sums over its slots; combine sums the per-destination partial
+ * outputs); NeMo "uccl_ep.buffer": Buffer.combine (topk_weights optional,
+ * bias: one tensor or a pair) / low_latency_combine; vLLM
  * BatchedPrepareAndFinalize.finalize; NeMo token_dispatcher
  * TokenDispatcherConfig.moe_router_dtype (fp32 for the weighted average).
  *
- *   out[t,:] = bf16( sum_{k=0..K-1, r = token_row[t,k] >= 0} w[t,k] * y[r,:] )
- * accumulated in fp32: each product is rounded to fp32, then added to the
- * running fp32 sum (starting at +0.0) in ascending k; the sum is rounded
+ * With topk_weights:
+ *   out[t,:] = bf16( sum_{k=0..K-1, r = token_row[t,k] >= 0} w[t,k] * y[r,:]
+ *                    + bias0[t,:] + bias1[t,:] )
+ * each product rounded to fp32, then added to the running fp32 sum (starting
+ * at +0.0) in ascending k.  Without (topk_weights == NULL): each distinct row
+ * of token t is added once, in the order of its first slot.  The biases that
+ * are given are added after the expert terms, bias0 first; the sum is rounded
  * once to bf16, to nearest with ties to even.  Rows r >= num_rows are
- * skipped.  Tokens with no row give +0.
+ * skipped.  Tokens with no row give +0 (plus the biases).
  *
  *   y             [num_rows, H] bf16 in   expert outputs (send rows, or the
  *                                         batched buffer viewed as rows)
  *   token_row     [T,K] int32 in
- *   topk_weights  [T,K] fp32 in
+ *   topk_weights  [T,K] fp32 in, or NULL for the unweighted partial sums
+ *   bias0, bias1  [T,H] bf16 in, or NULL (16-byte aligned)
  *   out           [T,H] bf16 out
  */
 int ep_combine(const void* y, int64_t num_rows, const int32_t* token_row,
                const float* topk_weights, int64_t num_tokens, int num_topk,
-               int hidden, void* out, hipStream_t stream);
+               int hidden, const void* bias0, const void* bias1, void* out,
+               hipStream_t stream);
 
 #ifdef __cplusplus
 }

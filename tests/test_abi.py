@@ -36,8 +36,9 @@ def test_library_exports_every_header_function():
 
 
 def test_version_and_status_strings():
+    # version 2: ep_combine takes optional weights and biases
     L = _lib.lib()
-    assert L.ep_abi_version() == 1
+    assert L.ep_abi_version() == 2
     assert L.ep_status_string(0) == b"ok"
     for s in (-1, -2, -3, -4):
         assert L.ep_status_string(s) not in (b"ok", b"unknown status")
@@ -137,10 +138,13 @@ def test_permute_and_combine_reject_bad_rows():
     assert perm(A8, 4, 64, A16, 2, 8, 0, A16, None, None) == _lib.EP_ERR_INVALID_ARG   # x align
     assert perm(A16, 4, 64, A16, 2, 8, 5, A16, None, None) == _lib.EP_ERR_INVALID_ARG  # dtype
     comb = L.ep_combine
-    assert comb(A16, 10, A16, A16, 4, 2, 60, A16, None) == _lib.EP_ERR_INVALID_ARG
-    assert comb(None, 10, A16, A16, 4, 2, 64, A16, None) == _lib.EP_ERR_INVALID_ARG
-    assert comb(A16, 10, A16, A16, 4, 0, 64, A16, None) == _lib.EP_ERR_INVALID_ARG
-    assert comb(A16, 10, A16, A16, 4, 2, 64, A8, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, A16, 4, 2, 60, None, None, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(None, 10, A16, A16, 4, 2, 64, None, None, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, A16, 4, 0, 64, None, None, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, A16, 4, 2, 64, None, None, A8, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, ODD, 4, 2, 64, None, None, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, A16, 4, 2, 64, A8, None, A16, None) == _lib.EP_ERR_INVALID_ARG
+    assert comb(A16, 10, A16, None, 4, 2, 64, A16, A8, A16, None) == _lib.EP_ERR_INVALID_ARG
 
 
 def test_batched_rejects_bad_arguments():
