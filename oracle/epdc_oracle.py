@@ -57,6 +57,7 @@ __all__ = [
     "dequantize_rows_fp8",
     "dispatch_permute_fp8",
     "batched_prepare",
+    "regroup_by_expert",
     "combine",
     "combine_partials",
     "FP8_MAX",
@@ -319,6 +320,62 @@ def batched_prepare(x_bits, topk_idx, first_expert, num_local_experts,
             b_x[e, slot] = x[t]
             token_row[t, hit_slots[t]] = e * M + slot
     return b_x, tokens_per_expert, token_row
+
+
+# --------------------------------------------------------------------------
+# Receive side: rows regrouped by local expert
+# --------------------------------------------------------------------------
+
+def regroup_by_expert(x_bits, recv_idx, recv_w, num_local_experts, align=1):
+    """[nemo] MoEFlexTokenDispatcher.dispatch_postprocess and
+    _DeepepManager.get_permuted_hidden_states_by_experts (the received rows
+    permuted so that each local expert's rows are contiguous, with the
+    number of tokens per expert); [nemo] TokenDispatcherConfig
+    moe_router_expert_pad_multiple and [uccl] Buffer.dispatch
+    expert_alignment (each expert's row count padded to a multiple).
+
+    For local expert e = 0..E_local-1 in order, each received row r whose
+    recv_idx names e (in ascending r) takes the next row of e's segment,
+    which is then padded with zero rows to a multiple of ``align``.
+    Returns perm_x [M,H] bf16 bits, perm_src [M] (the received row, -1 on
+    padding), perm_w [M] (that slot's weight, 0 on padding),
+    tokens_per_expert [E_local] (without padding), offsets [E_local+1]
+    (padded segment starts; offsets[E_local] = M) and row_map [R,K] (the
+    permuted row of slot k, -1 where the slot names no local expert).
+    """
+    x = np.asarray(x_bits, dtype=np.uint16)
+    idx = np.asarray(recv_idx, dtype=np.int64)
+    w = np.asarray(recv_w, dtype=np.float32)
+    R, K = idx.shape
+    H = x.shape[1]
+    El, A = int(num_local_experts), int(align)
+    if A < 1:
+        raise ValueError("align must be >= 1")
+    validate_routing(idx, El)
+    counts = np.zeros(El, dtype=np.int32)
+    members = []
+    for e in range(El):
+        rows = [r for r in range(R) if (idx[r] == e).any()]
+        members.append(rows)
+        counts[e] = len(rows)
+    padded = [-(-int(c) // A) * A for c in counts]
+    offsets = np.zeros(El + 1, dtype=np.int32)
+    for e in range(El):
+        offsets[e + 1] = offsets[e] + padded[e]
+    M = int(offsets[El])
+    perm_x = np.zeros((M, H), dtype=np.uint16)
+    perm_src = np.full(M, -1, dtype=np.int32)
+    perm_w = np.zeros(M, dtype=np.float32)
+    row_map = np.full((R, K), -1, dtype=np.int32)
+    for e in range(El):
+        for s, r in enumerate(members[e]):
+            n = offsets[e] + s
+            k = int(np.flatnonzero(idx[r] == e)[0])
+            perm_x[n] = x[r]
+            perm_src[n] = r
+            perm_w[n] = w[r, k]
+            row_map[r, k] = n
+    return perm_x, perm_src, perm_w, counts, offsets, row_map
 
 
 # --------------------------------------------------------------------------

@@ -47,6 +47,11 @@ ROUTING_PINS = [
     pin(RT, "test_layout_invariants_skewed"),
     pin(RT, "test_chunk_bounds_cases", GOLDEN),
 ]
+REGROUP_PINS = [
+    pin(RT, "test_regroup_equals_stable_sort_and_bincount", 4),
+    pin(RT, "test_regroup_brute_force_tiny"),
+    pin(RT, "test_regroup_restore_is_weighted_sum"),
+]
 PARTIAL_PINS = [
     pin(NUM, "test_combine_partials_counts_each_destination_once"),
     pin(NUM, "test_combine_partials_within_1ulp_of_exact_sum"),
@@ -127,6 +132,18 @@ MUTANTS = {
     "fp8_zero_group_sign": (
         "q = np.where((scale > 0)[:, :, None], q, np.uint8(0))",
         "q = np.where((scale > 0)[:, :, None], q, np.uint8(0x80))", FORMAT_PINS),
+    "regroup_no_padding": (
+        "    padded = [-(-int(c) // A) * A for c in counts]",
+        "    padded = [int(c) for c in counts]", REGROUP_PINS),
+    "regroup_rows_descending": (
+        "        rows = [r for r in range(R) if (idx[r] == e).any()]",
+        "        rows = [r for r in range(R - 1, -1, -1) if (idx[r] == e).any()]", REGROUP_PINS),
+    "regroup_weight_of_first_slot_wrong": (
+        "            perm_w[n] = w[r, k]",
+        "            perm_w[n] = w[r, 0]", REGROUP_PINS),
+    "regroup_offset_off_by_one": (
+        "            n = offsets[e] + s",
+        "            n = offsets[e] + s + (1 if e else 0)", REGROUP_PINS),
     "partials_duplicates_counted": (
         "            if r < 0 or r in seen:",
         "            if r < 0:", PARTIAL_PINS),
@@ -171,6 +188,6 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 def test_unmutated_copy_passes_all_pins(monkeypatch):
     mod = make_mutant("FP8_GROUP = 128", "FP8_GROUP = 128")
     for module, fn, args in (ROUTING_PINS + COMBINE_PINS + FORMAT_PINS + BATCHED_PINS +
-                             PARTIAL_PINS):
+                             PARTIAL_PINS + REGROUP_PINS):
         monkeypatch.setattr(module, "O", mod)
         getattr(module, fn)(*args)

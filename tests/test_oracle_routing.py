@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from epgen import balanced_routing, make_routing, spec, CONFIGS
+from epgen import CONFIGS, balanced_routing, make_hidden, make_routing, spec
 
 
 # --------------------------------------------------------------------------
@@ -289,3 +289,84 @@ def test_config_routing_invariants(name):
     dest, iir, sc, tpe = O.compute_send_counts(idx, P, s.E_local, s.chunks)
     assert int(sc.sum()) == int(iir.sum())
     assert int(tpe.sum()) == int((idx >= 0).sum())
+
+
+# --------------------------------------------------------------------------
+# receive-side regroup by local expert
+# --------------------------------------------------------------------------
+
+def _recv_segment(name="skewed_t16384", T=600, p=5, seed=0):
+    """The rows one destination receives: its send segment with K-wide local
+    ids (-1 elsewhere) and weights, as the send layout builds them."""
+    s = spec(name, T=T, H=16, seed=seed)
+    idx, w = make_routing(s)
+    rng = np.random.default_rng(seed)
+    x = rng.integers(0, 1 << 16, size=(s.T, s.H), dtype=np.uint16)
+    sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, s.P, s.E_local)
+    seg = srk == p
+    return x[sti[seg]], sidx[seg], sw[seg], s.E_local
+
+
+@pytest.mark.parametrize("align", [1, 4, 16, 128])
+def test_regroup_equals_stable_sort_and_bincount(align):
+    rx, ridx, rw, El = _recv_segment()
+    px, src, pw, cnt, off, rmap = O.regroup_by_expert(rx, ridx, rw, El, align)
+    r_all, k_all = np.nonzero(ridx >= 0)
+    e_all = ridx[r_all, k_all]
+    assert np.array_equal(cnt, np.bincount(e_all, minlength=El))
+    padded = -(-cnt // align) * align
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(padded)]))
+    order = np.lexsort((r_all, e_all))                   # expert, then row
+    rank = np.concatenate([np.arange(c) for c in cnt]) if len(cnt) else np.zeros(0)
+    want = off[e_all[order]] + rank
+    assert np.array_equal(rmap[r_all[order], k_all[order]], want)
+    assert np.all(rmap[ridx < 0] == -1)
+    assert np.array_equal(src[want], r_all[order])
+    assert np.array_equal(px[want], rx[r_all[order]])
+    assert np.array_equal(pw[want].view(np.uint32), rw[r_all[order], k_all[order]].view(np.uint32))
+    pad = np.ones(len(src), dtype=bool)
+    pad[want] = False
+    assert np.all(src[pad] == -1) and not px[pad].any() and not pw[pad].any()
+    assert len(src) == off[-1] and np.all(off % align == 0)
+
+
+def test_regroup_brute_force_tiny():
+    # 5 received rows, K=3, 3 local experts, alignment 2, worked by hand:
+    # e0 <- rows 0, 3 ; e1 <- rows 1, 3, 4 ; e2 <- row 2
+    ridx = np.array([[0, -1, -1], [-1, 1, -1], [2, -1, -1], [1, 0, -1], [-1, -1, 1]])
+    rw = np.arange(15, dtype=np.float32).reshape(5, 3) / 16
+    rx = np.arange(10, dtype=np.uint16).reshape(5, 2) + 1
+    px, src, pw, cnt, off, rmap = O.regroup_by_expert(rx, ridx, rw, 3, 2)
+    assert cnt.tolist() == [2, 3, 1]
+    assert off.tolist() == [0, 2, 6, 8]
+    assert src.tolist() == [0, 3, 1, 3, 4, -1, 2, -1]
+    assert pw.tolist() == [0 / 16, 10 / 16, 4 / 16, 9 / 16, 14 / 16, 0, 6 / 16, 0]
+    assert rmap.tolist() == [[0, -1, -1], [-1, 2, -1], [6, -1, -1], [3, 1, -1], [-1, -1, 4]]
+    assert px.tolist() == [[1, 2], [7, 8], [3, 4], [7, 8], [9, 10], [0, 0], [5, 6], [0, 0]]
+
+
+def test_regroup_restore_is_weighted_sum():
+    # an identity expert over the regrouped rows, restored by the weighted
+    # combine through row_map, gives each received row times its local weights
+    s = spec("uniform_t4096", T=400, H=32)
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, s.P, s.E_local)
+    seg = srk == 3
+    px, src, pw, cnt, off, rmap = O.regroup_by_expert(x[sti[seg]], sidx[seg], sw[seg],
+                                                      s.E_local, 8)
+    back = O.combine(px, rmap, sw[seg])
+    lw = sw[seg].astype(np.float64).sum(axis=1)[:, None]
+    exact = lw * O.bf16_to_f32(x[sti[seg]]).astype(np.float64)
+    got = O.bf16_to_f32(back).astype(np.float64)
+    ulp = np.maximum(np.abs(exact), 2.0 ** -126) * 2.0 ** -7
+    assert np.all(np.abs(got - exact) <= ulp)
+
+
+def test_regroup_rejects_bad_ids_and_alignment():
+    with pytest.raises(ValueError):
+        O.regroup_by_expert(np.zeros((1, 8), np.uint16), np.array([[3]]), np.ones((1, 1)), 3)
+    with pytest.raises(ValueError):
+        O.regroup_by_expert(np.zeros((1, 8), np.uint16), np.array([[1, 1]]), np.ones((1, 2)), 3)
+    with pytest.raises(ValueError):
+        O.regroup_by_expert(np.zeros((1, 8), np.uint16), np.array([[1]]), np.ones((1, 1)), 3, 0)
