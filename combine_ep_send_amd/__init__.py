@@ -20,10 +20,13 @@ from .dispatch import (  # noqa: F401
     compute_send_counts,
     dispatch,
     dispatch_chunked_forward,
+    permute_by_expert,
+    restore_by_expert,
     to_host,
 )
 from .ops import (  # noqa: F401
     Counts,
+    Regrouped,
     SendLayout,
     ep_batched_prepare,
     ep_batched_workspace_bytes,
@@ -35,5 +38,7 @@ from .ops import (  # noqa: F401
     ep_counts_workspace_bytes,
     ep_dispatch_permute,
     ep_layout_workspace_bytes,
+    ep_regroup_by_expert,
+    ep_regroup_workspace_bytes,
     workspace_for,
 )

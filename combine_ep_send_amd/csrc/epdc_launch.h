@@ -94,12 +94,31 @@ struct FusedArgs {
   uint32_t* rows;                // [groups, P + E + 1] published totals
   int64_t tiles;                 // tiles of 256 tokens (>= 1)
   int tiles_per_group;
+  // regroup by local expert (P = E_local bins, E = 0)
+  const int32_t* ids32;          // [R,K] local expert ids, -1 = not local
+  int align;                     // segment alignment (>= 1)
+  int32_t* offsets;              // [P+1] aligned segment starts
+  float* perm_w;                 // [cap] weight of each row's slot, or null
 };
 // Workgroups of the fused counts + layout launch: at most one per compute
 // unit and at most kMaxFusedGroups, so that all of them are resident at once.
 constexpr int kMaxFusedGroups = 256;
 size_t fused_smem_bytes(int P, int E, int tiles_per_group);
 hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
+hipError_t launch_regroup_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
+
+struct RegroupPadArgs {
+  const int32_t* counts;         // [E_local] rows per expert
+  const int32_t* offsets;        // [E_local+1] aligned starts
+  int E_local;
+  int align;
+  int64_t capacity;
+  int H;
+  void* perm_x;                  // [cap, H] bf16
+  int32_t* perm_src;             // [cap]
+  float* perm_w;                 // [cap] or null
+};
+hipError_t launch_regroup_pad(const RegroupPadArgs& a, hipStream_t s);
 
 struct RowArgs {
   const void* x;

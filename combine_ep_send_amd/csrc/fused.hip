@@ -18,6 +18,13 @@
 //
 // Against the two-call path this removes one launch and the tile-to-tile
 // lookback chain; only the barrier's round trip remains.
+//
+// The same kernel regroups received rows by local expert (NeMo
+// token_dispatcher: dispatch_postprocess / get_permuted_hidden_states_by_
+// experts; moe_router_expert_pad_multiple; uccl Buffer.dispatch
+// expert_alignment): the bins are the local expert ids themselves, each
+// expert's segment starts at the exclusive scan of the counts rounded up to
+// the alignment, and each row records its source row and its slot's weight.
 #include "epdc_device.h"
 #include "epdc_launch.h"
 
@@ -36,10 +43,31 @@ struct TileSlots {
   int bad;
 };
 
-template <int KMAX>
+enum { kFusedSend = 0, kFusedRegroup = 1 };
+
+template <int MODE, int KMAX>
 __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid,
                                        TileSlots<KMAX>& s) {
   s.bad = 0;
+  if (MODE == kFusedRegroup) {
+    // received rows: K-wide local expert ids (int32), the bin is the id
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      s.ids[k] = -1;
+      s.wts[k] = 0.0f;
+      s.bin[k] = -1;
+      if (valid && k < a.K) {
+        const int v = a.ids32[t * a.K + k];
+        s.ids[k] = v;
+        if (a.topk_weights) s.wts[k] = a.topk_weights[t * a.K + k];
+        if (v >= 0 && v < a.P)
+          s.bin[k] = v;
+        else if (v != -1)
+          ++s.bad;
+      }
+    }
+    return;
+  }
   if (valid && a.vec_in && a.K == KMAX) {
     // whole rows of ids and weights as 16-byte loads
     const u32x4* pi = reinterpret_cast<const u32x4*>(a.topk_idx + t * KMAX);
@@ -99,7 +127,7 @@ __device__ __forceinline__ void ballots(const TileSlots<KMAX>& s, int P, int wav
   }
 }
 
-template <int KMAX>
+template <int MODE, int KMAX>
 __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int P = a.P;
@@ -121,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   int64_t tile1 = tile0 + a.tiles_per_group;
   if (tile1 > a.tiles) tile1 = a.tiles;
   const int my_tiles = tile1 > tile0 ? int(tile1 - tile0) : 0;
-  const bool want_e = a.tokens_per_expert != nullptr;
+  const bool want_e = MODE == kFusedSend && a.tokens_per_expert != nullptr;
 
   // The barrier generation is read now and first used at the barrier, so
   // its round trip overlaps the decode.
@@ -135,8 +163,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   for (int j = 0; j < my_tiles; ++j) {
     const int64_t t = (tile0 + j) * kTile + tid;
     const bool valid = t < a.T;
-    decode<KMAX>(a, t, valid, sl);
-    if (valid) {
+    decode<MODE, KMAX>(a, t, valid, sl);
+    if (MODE == kFusedSend && valid) {
 #pragma unroll
       for (int k = 0; k < KMAX; ++k)
         if (k < a.K) a.dest[t * a.K + k] = sl.bin[k];
@@ -262,21 +290,27 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
     for (int b = tid; b < P; b += kBlock) a.send_counts[b] = s_tot[b];
     if (tid == 0 && a.diag) a.diag[0] = s_bad;
   }
-  // Segment starts (exclusive scan of the totals) added into the bases.
+  // Segment starts (exclusive scan of the totals, each rounded up to the
+  // alignment when regrouping) added into the bases.
   if (wave == 0) {
     int carry = 0;
     for (int b0 = 0; b0 < P; b0 += kWave) {
       const int b = b0 + lane;
-      const int v = b < P ? s_tot[b] : 0;
+      int v = b < P ? s_tot[b] : 0;
+      if (MODE == kFusedRegroup) v = (v + a.align - 1) / a.align * a.align;
       int incl = v;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const int u = __shfl_up(incl, off);
         if (lane >= off) incl += u;
       }
-      if (b < P) s_base[b] += carry + incl - v;
+      if (b < P) {
+        s_base[b] += carry + incl - v;
+        if (MODE == kFusedRegroup && g == 0) a.offsets[b] = carry + incl - v;
+      }
       carry += __shfl(incl, kWave - 1);
     }
+    if (MODE == kFusedRegroup && g == 0 && lane == 0) a.offsets[P] = carry;
   }
   __syncthreads();
 
@@ -286,7 +320,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
     const int64_t t = (tile0 + j) * kTile + tid;
     const bool valid = t < a.T;
     if (my_tiles > 1) {       // a single tile's slots are still in registers
-      decode<KMAX>(a, t, valid, sl);
+      decode<MODE, KMAX>(a, t, valid, sl);
       ballots<KMAX>(sl, P, wave, lane, s_bal);
     }
     __syncthreads();
@@ -323,6 +357,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
       if (!first) continue;
       const int b = sl.bin[k];
       const int32_t n = rowk[k];
+      if (MODE == kFusedRegroup) {          // source row and the slot's weight
+        a.send_token_idx[n] = int32_t(t);
+        if (a.perm_w) a.perm_w[n] = sl.wts[k];
+        continue;
+      }
       a.send_token_idx[n] = int32_t(t);
       a.send_rank[n] = b;
       const int64_t ob = int64_t(b) * a.E_local;
@@ -368,15 +407,24 @@ size_t fused_smem_bytes(int P, int E, int tiles_per_group) {
          size_t(tiles_per_group) * P * 4 + size_t(P + E + 1) * 4;
 }
 
-hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s) {
+template <int MODE>
+hipError_t launch_fused(const FusedArgs& a, unsigned groups, hipStream_t s) {
   const size_t smem = fused_smem_bytes(a.P, a.E, a.tiles_per_group);
   if (a.K <= 4)
-    dispatch_layout_kernel<4><<<groups, kBlock, smem, s>>>(a);
+    dispatch_layout_kernel<MODE, 4><<<groups, kBlock, smem, s>>>(a);
   else if (a.K <= 8)
-    dispatch_layout_kernel<8><<<groups, kBlock, smem, s>>>(a);
+    dispatch_layout_kernel<MODE, 8><<<groups, kBlock, smem, s>>>(a);
   else
-    dispatch_layout_kernel<16><<<groups, kBlock, smem, s>>>(a);
+    dispatch_layout_kernel<MODE, 16><<<groups, kBlock, smem, s>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s) {
+  return launch_fused<kFusedSend>(a, groups, s);
+}
+
+hipError_t launch_regroup_layout(const FusedArgs& a, unsigned groups, hipStream_t s) {
+  return launch_fused<kFusedRegroup>(a, groups, s);
 }
 
 }  // namespace epdc

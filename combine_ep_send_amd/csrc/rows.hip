@@ -203,6 +203,31 @@ __global__ __launch_bounds__(kBlock) void zero_pad_kernel(PadArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Padding rows of the regrouped layout: expert e's rows [offsets[e] +
+// counts[e], offsets[e+1]) (fewer than `align`) become zero rows with source
+// -1 and weight 0.  Grid (chunks of the padding pieces, E_local).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void regroup_pad_kernel(RegroupPadArgs a) {
+  const int e = blockIdx.y;
+  const int64_t H8 = a.H >> 3;
+  const int64_t start = int64_t(a.offsets[e]) + a.counts[e];
+  int64_t end = a.offsets[e + 1];
+  if (end > a.capacity) end = a.capacity;
+  const int64_t n = (end - start) * H8;
+  u32x4* px = static_cast<u32x4*>(a.perm_x);
+  for (int64_t v = int64_t(blockIdx.x) * kBlock + threadIdx.x; v < n;
+       v += int64_t(gridDim.x) * kBlock) {
+    const int64_t r = start + v / H8;
+    const int64_t j = v - (v / H8) * H8;
+    px[r * H8 + j] = u32x4{0u, 0u, 0u, 0u};
+    if (j == 0) {
+      a.perm_src[r] = -1;
+      if (a.perm_w) a.perm_w[r] = 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Combine.  Weighted: out[t] = bf16( sum_k w[t,k] * y[token_row[t,k]] ), the
 // fp32 product rounded, then added in ascending k (no contraction into FMA).
 // Unweighted (no weights given): each distinct row of t, i.e. each
@@ -403,6 +428,15 @@ hipError_t launch_zero_pad(const PadArgs& a, hipStream_t s) {
   const int64_t gx = (region + kBlock - 1) / kBlock;
   const dim3 grid{unsigned(gx < kMaxGrid ? gx : kMaxGrid), unsigned(a.E_local), 1u};
   zero_pad_kernel<<<grid, kBlock, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_regroup_pad(const RegroupPadArgs& a, hipStream_t s) {
+  if (a.align <= 1 || a.E_local == 0) return hipSuccess;
+  const int64_t pieces = int64_t(a.align - 1) * (a.H >> 3);
+  const int64_t gx = (pieces + kBlock - 1) / kBlock;
+  const dim3 grid{unsigned(gx < 4096 ? gx : 4096), unsigned(a.E_local), 1u};
+  regroup_pad_kernel<<<grid, kBlock, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -12,8 +12,9 @@ from typing import Callable, List, NamedTuple, Optional, Tuple
 
 import torch
 
-from .ops import (ep_batched_prepare, ep_build_send_layout, ep_combine,
-                  ep_compute_send_counts, ep_dispatch_layout, ep_dispatch_permute)
+from .ops import (Regrouped, ep_batched_prepare, ep_build_send_layout, ep_combine,
+                  ep_compute_send_counts, ep_dispatch_layout, ep_dispatch_permute,
+                  ep_regroup_by_expert)
 
 __all__ = [
     "chunk_bounds",
@@ -26,6 +27,8 @@ __all__ = [
     "dispatch_chunked_forward",
     "batched_prepare",
     "batched_finalize",
+    "permute_by_expert",
+    "restore_by_expert",
 ]
 
 
@@ -207,3 +210,28 @@ def batched_finalize(fused_expert_output: torch.Tensor, topk_weights: torch.Tens
     """vLLM BatchedPrepareAndFinalize.finalize: weight by topk_weights and sum
     the local experts' outputs per token (fp32 accumulation)."""
     return ep_combine(fused_expert_output, token_row, topk_weights, out=out)
+
+
+def permute_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
+                      recv_w: Optional[torch.Tensor], *, num_local_experts: int,
+                      pad_multiple: int = 1) -> Regrouped:
+    """The received rows regrouped so that each local expert's rows are
+    contiguous, each expert padded to ``pad_multiple`` rows (NeMo
+    get_permuted_hidden_states_by_experts / dispatch_postprocess with
+    moe_router_expert_pad_multiple; Buffer.dispatch expert_alignment).
+    ``recv_idx`` holds local expert ids (-1 elsewhere), e.g. the send_idx of
+    one destination's segment; an int64 tensor is converted."""
+    if recv_idx.dtype != torch.int32:
+        recv_idx = recv_idx.to(torch.int32)
+    return ep_regroup_by_expert(recv_x, recv_idx.contiguous(), recv_w, num_local_experts,
+                                pad_multiple)
+
+
+def restore_by_expert(expert_out: torch.Tensor, regrouped: Regrouped,
+                      recv_w: Optional[torch.Tensor], out: Optional[torch.Tensor] = None
+                      ) -> torch.Tensor:
+    """Expert outputs [rows, H] in the regrouped order back onto the received
+    rows (NeMo get_restored_hidden_states_by_experts): weighted by ``recv_w``
+    and summed over each row's local slots, or, with ``recv_w=None``, summed
+    unweighted."""
+    return ep_combine(expert_out, regrouped.row_map, recv_w, out=out)

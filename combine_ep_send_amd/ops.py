@@ -23,6 +23,9 @@ __all__ = [
     "ep_dispatch_layout",
     "ep_dispatch_layout_workspace_bytes",
     "ep_dispatch_permute",
+    "ep_regroup_by_expert",
+    "ep_regroup_workspace_bytes",
+    "Regrouped",
     "ep_batched_prepare",
     "ep_combine",
     "ep_counts_workspace_bytes",
@@ -46,6 +49,15 @@ class SendLayout(NamedTuple):
     send_idx: torch.Tensor             # int32 [cap, K]
     send_w: torch.Tensor               # float32 [cap, K]
     token_row: torch.Tensor            # int32 [T, K]
+
+
+class Regrouped(NamedTuple):
+    perm_x: torch.Tensor               # bf16 [cap, H]
+    perm_src: torch.Tensor             # int32 [cap]: received row, -1 on padding
+    perm_w: Optional[torch.Tensor]     # float32 [cap]: the slot's weight
+    tokens_per_expert: torch.Tensor    # int32 [E_local]
+    expert_offsets: torch.Tensor       # int32 [E_local + 1]
+    row_map: torch.Tensor              # int32 [R, K]
 
 
 def _vp(t: Optional[torch.Tensor]):
@@ -261,6 +273,65 @@ def ep_dispatch_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor, num_r
         _stream(stream))
     check(st, "ep_dispatch_layout")
     return counts, out
+
+
+def ep_regroup_workspace_bytes(num_rows: int, num_local_experts: int) -> int:
+    return int(lib().ep_regroup_workspace_bytes(int(num_rows), int(num_local_experts)))
+
+
+def ep_regroup_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
+                         recv_w: Optional[torch.Tensor], num_local_experts: int,
+                         align: int = 1, capacity: Optional[int] = None, *,
+                         out: Optional[Regrouped] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> Regrouped:
+    """Received rows regrouped by local expert, each expert's segment padded
+    to a multiple of ``align``.  The default capacity is the worst case
+    R*min(K, E_local) + E_local*(align-1); the real row count is
+    ``expert_offsets[-1]``."""
+    _gpu(recv_x, "recv_x", torch.bfloat16, 2)
+    R, H = recv_x.shape
+    _gpu(recv_idx, "recv_idx", torch.int32, 2)
+    if recv_idx.shape[0] != R:
+        raise ValueError("recv_idx must be [R, K]")
+    K = recv_idx.shape[1]
+    El, A = int(num_local_experts), int(align)
+    if recv_w is not None:
+        _shape(_gpu(recv_w, "recv_w", torch.float32), "recv_w", (R, K))
+    cap = R * min(K, El) + El * (A - 1) if capacity is None else int(capacity)
+    dev = recv_x.device
+    if out is None:
+        out = Regrouped(
+            perm_x=torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
+            perm_src=torch.empty(cap, dtype=torch.int32, device=dev),
+            perm_w=(torch.empty(cap, dtype=torch.float32, device=dev)
+                    if recv_w is not None else None),
+            tokens_per_expert=torch.empty(El, dtype=torch.int32, device=dev),
+            expert_offsets=torch.empty(El + 1, dtype=torch.int32, device=dev),
+            row_map=torch.empty((R, K), dtype=torch.int32, device=dev))
+    _gpu(out.perm_x, "perm_x", torch.bfloat16, 2)
+    if out.perm_x.shape[0] < cap or out.perm_x.shape[1] != H:
+        raise ValueError(f"perm_x must be [>= {cap}, {H}]")
+    _gpu(out.perm_src, "perm_src", torch.int32)
+    if out.perm_src.numel() < cap:
+        raise ValueError("perm_src holds fewer rows than the capacity")
+    if out.perm_w is not None:
+        _gpu(out.perm_w, "perm_w", torch.float32)
+        if out.perm_w.numel() < cap:
+            raise ValueError("perm_w holds fewer rows than the capacity")
+    _shape(_gpu(out.tokens_per_expert, "tokens_per_expert", torch.int32), "tokens_per_expert",
+           (El,))
+    _shape(_gpu(out.expert_offsets, "expert_offsets", torch.int32), "expert_offsets", (El + 1,))
+    _shape(_gpu(out.row_map, "row_map", torch.int32), "row_map", (R, K))
+    if workspace is None:
+        workspace = workspace_for(ep_regroup_workspace_bytes(R, El), dev, stream, "fused")
+    _gpu(workspace, "workspace", torch.uint8)
+    st = lib().ep_regroup_by_expert(
+        _vp(recv_x), _vp(recv_idx), _vp(recv_w), R, K, H, El, A, cap, _vp(out.perm_x),
+        _vp(out.perm_src), _vp(out.perm_w), _vp(out.tokens_per_expert),
+        _vp(out.expert_offsets), _vp(out.row_map), _vp(workspace), workspace.numel(),
+        _stream(stream))
+    check(st, "ep_regroup_by_expert")
+    return out
 
 
 def ep_dispatch_permute(x: torch.Tensor, token_row: torch.Tensor, num_send_capacity: int, *,

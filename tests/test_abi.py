@@ -17,6 +17,7 @@ EXPECTED = {
     "ep_abi_version", "ep_status_string", "ep_counts_workspace_bytes", "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
     "ep_dispatch_layout_workspace_bytes", "ep_dispatch_layout",
+    "ep_regroup_workspace_bytes", "ep_regroup_by_expert",
     "ep_dispatch_permute", "ep_batched_prepare", "ep_combine",
 }
 
@@ -127,6 +128,28 @@ def test_fused_layout_workspace_and_arguments():
     assert call(ws_bytes=64) == _lib.EP_ERR_WORKSPACE
     # LDS share over 64 KiB (1024 destinations x 8 experts): use the two calls
     assert call(P=1024, El=8) == _lib.EP_ERR_UNSUPPORTED
+
+
+def test_regroup_workspace_and_arguments():
+    L = _lib.lib()
+    assert L.ep_regroup_workspace_bytes(1000, 8) == 256 + 4 * (8 + 1) * 4
+    assert L.ep_regroup_workspace_bytes(0, 8) == 256 + 1 * 9 * 4
+    assert L.ep_regroup_workspace_bytes(10, 0) == 0
+    f = L.ep_regroup_by_expert
+
+    def call(R=16, K=2, H=64, El=4, align=1, cap=64, x=A16, idx=A16, ws=A16,
+             ws_bytes=1 << 20):
+        return f(x, idx, None, R, K, H, El, align, cap, A16, A16, None, A16, A16, A16, ws,
+                 ws_bytes, None)
+    assert call(align=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(El=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(cap=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(H=60) == _lib.EP_ERR_INVALID_ARG
+    assert call(x=A8) == _lib.EP_ERR_INVALID_ARG
+    assert call(idx=ODD) == _lib.EP_ERR_INVALID_ARG
+    assert call(El=2000) == _lib.EP_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.EP_ERR_WORKSPACE
+    assert call(ws_bytes=8) == _lib.EP_ERR_WORKSPACE
 
 
 def test_permute_and_combine_reject_bad_rows():
