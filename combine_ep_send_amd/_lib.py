@@ -39,8 +39,8 @@ _SIGNATURES = {
                _P, _SZ, _P]),
     "ep_regroup_workspace_bytes": (_SZ, [_I64, _I32]),
     "ep_regroup_by_expert": (
-        _I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P,
-               _SZ, _P]),
+        _I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P,
+               _P, _P, _SZ, _P]),
     "ep_dispatch_permute": (_I32, [_P, _I64, _I32, _P, _I32, _I64, _I32, _P, _P, _P]),
     "ep_batched_prepare": (
         _I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),

@@ -243,26 +243,28 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
   return launch_status(launch_dispatch_layout(a, unsigned(groups), stream));
 }
 
-size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_local_experts) {
-  if (num_rows < 0 || num_local_experts < 1) return 0;
+size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins) {
+  if (num_rows < 0 || num_bins < 1) return 0;
   const int64_t groups = fused_tiles(num_rows) < kMaxFusedGroups ? fused_tiles(num_rows)
                                                                   : kMaxFusedGroups;
-  return kWsHeaderBytes + size_t(groups) * size_t(num_local_experts + 1) * 4u;
+  return kWsHeaderBytes + size_t(groups) * size_t(num_bins + 1) * 4u;
 }
 
 int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const float* recv_w,
-                         int64_t num_rows, int num_topk, int hidden, int num_local_experts,
-                         int align, int64_t capacity, void* perm_x, int32_t* perm_src,
-                         float* perm_w, int32_t* tokens_per_expert, int32_t* expert_offsets,
-                         int32_t* row_map, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
-  if (num_rows < 0 || num_topk < 1 || num_local_experts < 1 || align < 1 || capacity < 0)
+                         const int32_t* row_group, int num_groups, int64_t num_rows,
+                         int num_topk, int hidden, int num_local_experts, int align,
+                         int64_t capacity, void* perm_x, int32_t* perm_src, float* perm_w,
+                         int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* row_map,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_rows < 0 || num_topk < 1 || num_local_experts < 1 || align < 1 || capacity < 0 ||
+      num_groups < 1 || (num_groups > 1 && !row_group && num_rows > 0))
     return EP_ERR_INVALID_ARG;
-  if (num_rows >= kMaxTokens || num_topk > EPDC_MAX_TOPK ||
-      num_local_experts > EPDC_MAX_BINS || num_rows * num_topk > INT32_MAX)
+  const int64_t bins64 = int64_t(num_groups) * num_local_experts;
+  if (num_rows >= kMaxTokens || num_topk > EPDC_MAX_TOPK || bins64 > EPDC_MAX_BINS ||
+      num_rows * num_topk > INT32_MAX)
     return EP_ERR_UNSUPPORTED;
-  if (capacity > INT32_MAX || int64_t(align) * num_local_experts > INT32_MAX)
-    return EP_ERR_UNSUPPORTED;
+  const int bins = int(bins64);
+  if (capacity > INT32_MAX || int64_t(align) * bins > INT32_MAX) return EP_ERR_UNSUPPORTED;
   int st = check_hidden(hidden, false);
   if (st != EP_OK) return st;
   const int64_t RK = num_rows * num_topk;
@@ -270,21 +272,21 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
       (recv_w && !aligned(recv_w, 4)) || !arr_ok(perm_x, capacity, 16) ||
       !arr_ok(perm_src, capacity, 4) || (perm_w && !aligned(perm_w, 4)) ||
       !arr_ok(tokens_per_expert, 1, 4) || !arr_ok(expert_offsets, 1, 4) ||
-      !arr_ok(row_map, RK, 4))
+      !arr_ok(row_map, RK, 4) || (row_group && !aligned(row_group, 4)))
     return EP_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, 256) ||
-      workspace_bytes < ep_regroup_workspace_bytes(num_rows, num_local_experts))
+      workspace_bytes < ep_regroup_workspace_bytes(num_rows, bins))
     return EP_ERR_WORKSPACE;
   const int64_t tiles = fused_tiles(num_rows);
   constexpr size_t kSmemLimit = 64 * 1024;
-  if (fused_smem_bytes(num_local_experts, 0,
-                       int((tiles + kMaxFusedGroups - 1) / kMaxFusedGroups)) > kSmemLimit)
+  if (fused_smem_bytes(bins, 0, int((tiles + kMaxFusedGroups - 1) / kMaxFusedGroups)) >
+      kSmemLimit)
     return EP_ERR_UNSUPPORTED;
   int64_t gmax = device_cus();
   if (gmax > kMaxFusedGroups) gmax = kMaxFusedGroups;
   const int64_t per = (tiles + gmax - 1) / gmax;
   const int64_t groups = (tiles + per - 1) / per;
-  if (fused_smem_bytes(num_local_experts, 0, int(per)) > kSmemLimit) return EP_ERR_UNSUPPORTED;
+  if (fused_smem_bytes(bins, 0, int(per)) > kSmemLimit) return EP_ERR_UNSUPPORTED;
 
   // 1. one launch: counts per local expert, aligned offsets, row_map, the
   //    source row and weight of every regrouped row
@@ -292,9 +294,10 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   a.topk_weights = recv_w;
   a.T = num_rows;
   a.K = num_topk;
-  a.P = num_local_experts;
-  a.E_local = 1;
+  a.P = bins;
+  a.E_local = num_local_experts;
   a.E = 0;
+  a.row_group = num_groups > 1 ? row_group : nullptr;
   a.capacity = capacity;
   a.send_counts = tokens_per_expert;
   a.send_token_idx = perm_src;
@@ -313,7 +316,7 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   RegroupPadArgs z{};
   z.counts = tokens_per_expert;
   z.offsets = expert_offsets;
-  z.E_local = num_local_experts;
+  z.E_local = bins;
   z.align = align;
   z.capacity = capacity;
   z.H = hidden;

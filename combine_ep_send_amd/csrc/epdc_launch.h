@@ -96,6 +96,7 @@ struct FusedArgs {
   int tiles_per_group;
   // regroup by local expert (P = E_local bins, E = 0)
   const int32_t* ids32;          // [R,K] local expert ids, -1 = not local
+  const int32_t* row_group;      // [R] receive buffer of each row, or null (P = groups*E_local)
   int align;                     // segment alignment (>= 1)
   int32_t* offsets;              // [P+1] aligned segment starts
   float* perm_w;                 // [cap] weight of each row's slot, or null

@@ -50,7 +50,11 @@ __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid
                                        TileSlots<KMAX>& s) {
   s.bad = 0;
   if (MODE == kFusedRegroup) {
-    // received rows: K-wide local expert ids (int32), the bin is the id
+    // received rows: K-wide local expert ids (int32); the bin is the id,
+    // offset by the row's group (the receive buffer it came from) when rows
+    // of several buffers are laid end to end
+    const int gbase = (valid && a.row_group) ? a.row_group[t] * a.E_local : 0;
+    const bool gok = !a.row_group || (gbase >= 0 && gbase < a.P);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       s.ids[k] = -1;
@@ -60,8 +64,8 @@ __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid
         const int v = a.ids32[t * a.K + k];
         s.ids[k] = v;
         if (a.topk_weights) s.wts[k] = a.topk_weights[t * a.K + k];
-        if (v >= 0 && v < a.P)
-          s.bin[k] = v;
+        if (v >= 0 && v < a.E_local && gok)
+          s.bin[k] = gbase + v;
         else if (v != -1)
           ++s.bad;
       }

@@ -214,17 +214,20 @@ def batched_finalize(fused_expert_output: torch.Tensor, topk_weights: torch.Tens
 
 def permute_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
                       recv_w: Optional[torch.Tensor], *, num_local_experts: int,
-                      pad_multiple: int = 1) -> Regrouped:
+                      pad_multiple: int = 1, row_group: Optional[torch.Tensor] = None,
+                      num_groups: int = 1) -> Regrouped:
     """The received rows regrouped so that each local expert's rows are
     contiguous, each expert padded to ``pad_multiple`` rows (NeMo
     get_permuted_hidden_states_by_experts / dispatch_postprocess with
     moe_router_expert_pad_multiple; Buffer.dispatch expert_alignment).
     ``recv_idx`` holds local expert ids (-1 elsewhere), e.g. the send_idx of
-    one destination's segment; an int64 tensor is converted."""
+    one destination's segment; an int64 tensor is converted.  With
+    ``row_group`` (e.g. the send layout's send_rank) every destination's
+    segment is regrouped at once, one after the other."""
     if recv_idx.dtype != torch.int32:
         recv_idx = recv_idx.to(torch.int32)
     return ep_regroup_by_expert(recv_x, recv_idx.contiguous(), recv_w, num_local_experts,
-                                pad_multiple)
+                                pad_multiple, row_group=row_group, num_groups=num_groups)
 
 
 def restore_by_expert(expert_out: torch.Tensor, regrouped: Regrouped,

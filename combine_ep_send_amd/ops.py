@@ -275,18 +275,21 @@ def ep_dispatch_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor, num_r
     return counts, out
 
 
-def ep_regroup_workspace_bytes(num_rows: int, num_local_experts: int) -> int:
-    return int(lib().ep_regroup_workspace_bytes(int(num_rows), int(num_local_experts)))
+def ep_regroup_workspace_bytes(num_rows: int, num_bins: int) -> int:
+    return int(lib().ep_regroup_workspace_bytes(int(num_rows), int(num_bins)))
 
 
 def ep_regroup_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
                          recv_w: Optional[torch.Tensor], num_local_experts: int,
                          align: int = 1, capacity: Optional[int] = None, *,
+                         row_group: Optional[torch.Tensor] = None, num_groups: int = 1,
                          out: Optional[Regrouped] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> Regrouped:
     """Received rows regrouped by local expert, each expert's segment padded
-    to a multiple of ``align``.  The default capacity is the worst case
-    R*min(K, E_local) + E_local*(align-1); the real row count is
+    to a multiple of ``align``; with ``row_group`` ([R] int32, values in
+    [0, num_groups)) the rows are several receive buffers end to end and the
+    bins are (group, expert).  The default capacity is the worst case
+    R*min(K, E_local) + bins*(align-1); the real row count is
     ``expert_offsets[-1]``."""
     _gpu(recv_x, "recv_x", torch.bfloat16, 2)
     R, H = recv_x.shape
@@ -294,10 +297,15 @@ def ep_regroup_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
     if recv_idx.shape[0] != R:
         raise ValueError("recv_idx must be [R, K]")
     K = recv_idx.shape[1]
-    El, A = int(num_local_experts), int(align)
+    El, A, G = int(num_local_experts), int(align), int(num_groups)
+    B = G * El
     if recv_w is not None:
         _shape(_gpu(recv_w, "recv_w", torch.float32), "recv_w", (R, K))
-    cap = R * min(K, El) + El * (A - 1) if capacity is None else int(capacity)
+    if row_group is not None:
+        _shape(_gpu(row_group, "row_group", torch.int32), "row_group", (R,))
+    elif G != 1:
+        raise ValueError("num_groups > 1 needs row_group")
+    cap = R * min(K, El) + B * (A - 1) if capacity is None else int(capacity)
     dev = recv_x.device
     if out is None:
         out = Regrouped(
@@ -305,8 +313,8 @@ def ep_regroup_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
             perm_src=torch.empty(cap, dtype=torch.int32, device=dev),
             perm_w=(torch.empty(cap, dtype=torch.float32, device=dev)
                     if recv_w is not None else None),
-            tokens_per_expert=torch.empty(El, dtype=torch.int32, device=dev),
-            expert_offsets=torch.empty(El + 1, dtype=torch.int32, device=dev),
+            tokens_per_expert=torch.empty(B, dtype=torch.int32, device=dev),
+            expert_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev),
             row_map=torch.empty((R, K), dtype=torch.int32, device=dev))
     _gpu(out.perm_x, "perm_x", torch.bfloat16, 2)
     if out.perm_x.shape[0] < cap or out.perm_x.shape[1] != H:
@@ -319,14 +327,15 @@ def ep_regroup_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
         if out.perm_w.numel() < cap:
             raise ValueError("perm_w holds fewer rows than the capacity")
     _shape(_gpu(out.tokens_per_expert, "tokens_per_expert", torch.int32), "tokens_per_expert",
-           (El,))
-    _shape(_gpu(out.expert_offsets, "expert_offsets", torch.int32), "expert_offsets", (El + 1,))
+           (B,))
+    _shape(_gpu(out.expert_offsets, "expert_offsets", torch.int32), "expert_offsets", (B + 1,))
     _shape(_gpu(out.row_map, "row_map", torch.int32), "row_map", (R, K))
     if workspace is None:
-        workspace = workspace_for(ep_regroup_workspace_bytes(R, El), dev, stream, "fused")
+        workspace = workspace_for(ep_regroup_workspace_bytes(R, B), dev, stream, "fused")
     _gpu(workspace, "workspace", torch.uint8)
     st = lib().ep_regroup_by_expert(
-        _vp(recv_x), _vp(recv_idx), _vp(recv_w), R, K, H, El, A, cap, _vp(out.perm_x),
+        _vp(recv_x), _vp(recv_idx), _vp(recv_w), _vp(row_group), G, R, K, H, El, A, cap,
+        _vp(out.perm_x),
         _vp(out.perm_src), _vp(out.perm_w), _vp(out.tokens_per_expert),
         _vp(out.expert_offsets), _vp(out.row_map), _vp(workspace), workspace.numel(),
         _stream(stream))

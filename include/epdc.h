@@ -226,11 +226,11 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights,
 
 /*
  * Bytes of workspace ep_regroup_by_expert needs for R received rows and
- * E_local local experts: a 256-byte header (as ep_dispatch_layout's) and one
- * row of E_local + 1 uint32 per workgroup, min(ceil(R/256), 256) rows.  Same
- * zero-once / no-overlap rules.
+ * num_bins = num_groups * E_local bins: a 256-byte header (as
+ * ep_dispatch_layout's) and one row of num_bins + 1 uint32 per workgroup,
+ * min(ceil(R/256), 256) rows.  Same zero-once / no-overlap rules.
  */
-size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_local_experts);
+size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins);
 
 /*
  * Receive side: the received rows regrouped so that each local expert's rows
@@ -240,34 +240,41 @@ size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_local_experts);
  * TokenDispatcherConfig.moe_router_expert_pad_multiple; NeMo
  * "uccl_ep.buffer": Buffer.dispatch expert_alignment.
  *
- * For e = 0..E_local-1 in order, every row r whose recv_idx names e (in
- * ascending r) takes the next row of e's segment; the segment then gets
- * zero rows up to a multiple of align.  The inverse (expert outputs back to
- * the received rows) is ep_combine with token_row = row_map and the
- * received weights (or none).
+ * The rows may be several receive buffers laid end to end (on one GPU: the
+ * P destination segments of a send buffer): row_group[r] in
+ * [0, num_groups) names the buffer of row r, and the bins are (group, local
+ * expert), group-major; with num_groups == 1 row_group may be NULL.  For
+ * every bin in order, each row r of its group whose recv_idx names its
+ * expert (in ascending r) takes the next row of the bin's segment; the
+ * segment then gets zero rows up to a multiple of align.  So the result is
+ * the regroups of the buffers one after the other.  The inverse (expert
+ * outputs back to the received rows) is ep_combine with token_row = row_map
+ * and the received weights (or none).
  *
  *   recv_x        [R,H] bf16 in
  *   recv_idx      [R,K] int32 in   local expert ids, -1 = not local;
- *                                  other values are ignored like -1
+ *                                  values outside [-1, E_local) are ignored
  *   recv_w        [R,K] fp32 in, or NULL (then perm_w may be NULL too)
+ *   row_group     [R] int32 in, or NULL when num_groups == 1
  *   align         >= 1
  *   capacity      rows perm_x / perm_src / perm_w hold; rows past it are
  *                 not written and their slots get row_map -1
- *                 (R*min(K,E_local) + E_local*(align-1) always suffices)
- *   perm_x        [capacity,H] bf16 out   rows past offsets[E_local] untouched
+ *                 (R*min(K,E_local) + bins*(align-1) always suffices)
+ *   perm_x        [capacity,H] bf16 out   rows past offsets[bins] untouched
  *   perm_src      [capacity] int32 out    source row, -1 on padding
  *   perm_w        [capacity] fp32 out     the slot's weight, 0 on padding
  *                                         (may be NULL)
- *   tokens_per_expert [E_local] int32 out rows per expert, without padding
- *   expert_offsets    [E_local+1] int32 out aligned segment starts; the last
+ *   tokens_per_expert [bins] int32 out    rows per bin, without padding
+ *   expert_offsets    [bins+1] int32 out  aligned segment starts; the last
  *                                         entry is the total row count
  *   row_map       [R,K] int32 out  regrouped row of each local slot, else -1
- *   workspace     ep_regroup_workspace_bytes(R, E_local) bytes
+ *   workspace     ep_regroup_workspace_bytes(R, bins) bytes
  * One launch with a grid barrier (as ep_dispatch_layout: same time-out and
  * EP_ERR_UNSUPPORTED rule), then a padding kernel and the row permute.
  */
 int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx,
-                         const float* recv_w, int64_t num_rows, int num_topk,
+                         const float* recv_w, const int32_t* row_group,
+                         int num_groups, int64_t num_rows, int num_topk,
                          int hidden, int num_local_experts, int align,
                          int64_t capacity, void* perm_x, int32_t* perm_src,
                          float* perm_w, int32_t* tokens_per_expert,

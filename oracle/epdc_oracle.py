@@ -326,7 +326,8 @@ def batched_prepare(x_bits, topk_idx, first_expert, num_local_experts,
 # Receive side: rows regrouped by local expert
 # --------------------------------------------------------------------------
 
-def regroup_by_expert(x_bits, recv_idx, recv_w, num_local_experts, align=1):
+def regroup_by_expert(x_bits, recv_idx, recv_w, num_local_experts, align=1,
+                      row_group=None, num_groups=1):
     """[nemo] MoEFlexTokenDispatcher.dispatch_postprocess and
     _DeepepManager.get_permuted_hidden_states_by_experts (the received rows
     permuted so that each local expert's rows are contiguous, with the
@@ -342,6 +343,11 @@ def regroup_by_expert(x_bits, recv_idx, recv_w, num_local_experts, align=1):
     tokens_per_expert [E_local] (without padding), offsets [E_local+1]
     (padded segment starts; offsets[E_local] = M) and row_map [R,K] (the
     permuted row of slot k, -1 where the slot names no local expert).
+
+    With ``row_group`` the rows are ``num_groups`` receive buffers laid end to
+    end (on one GPU: the destination segments of a send buffer) and the bins
+    are (group g, expert e) in g-major order, each regrouped as above; the
+    counts and offsets then have num_groups*E_local (+1) entries.
     """
     x = np.asarray(x_bits, dtype=np.uint16)
     idx = np.asarray(recv_idx, dtype=np.int64)
@@ -352,24 +358,33 @@ def regroup_by_expert(x_bits, recv_idx, recv_w, num_local_experts, align=1):
     if A < 1:
         raise ValueError("align must be >= 1")
     validate_routing(idx, El)
-    counts = np.zeros(El, dtype=np.int32)
+    G = int(num_groups)
+    grp = np.zeros(R, dtype=np.int64) if row_group is None else np.asarray(row_group)
+    if row_group is None and G != 1:
+        raise ValueError("num_groups > 1 needs row_group")
+    if R and (grp.min() < 0 or grp.max() >= G):
+        raise ValueError("row_group outside [0, num_groups)")
+    B = G * El
+    counts = np.zeros(B, dtype=np.int32)
     members = []
-    for e in range(El):
-        rows = [r for r in range(R) if (idx[r] == e).any()]
+    for b in range(B):
+        g, e = divmod(b, El)
+        rows = [r for r in range(R) if grp[r] == g and (idx[r] == e).any()]
         members.append(rows)
-        counts[e] = len(rows)
+        counts[b] = len(rows)
     padded = [-(-int(c) // A) * A for c in counts]
-    offsets = np.zeros(El + 1, dtype=np.int32)
-    for e in range(El):
-        offsets[e + 1] = offsets[e] + padded[e]
-    M = int(offsets[El])
+    offsets = np.zeros(B + 1, dtype=np.int32)
+    for b in range(B):
+        offsets[b + 1] = offsets[b] + padded[b]
+    M = int(offsets[B])
     perm_x = np.zeros((M, H), dtype=np.uint16)
     perm_src = np.full(M, -1, dtype=np.int32)
     perm_w = np.zeros(M, dtype=np.float32)
     row_map = np.full((R, K), -1, dtype=np.int32)
-    for e in range(El):
-        for s, r in enumerate(members[e]):
-            n = offsets[e] + s
+    for b in range(B):
+        e = b % El
+        for s, r in enumerate(members[b]):
+            n = offsets[b] + s
             k = int(np.flatnonzero(idx[r] == e)[0])
             perm_x[n] = x[r]
             perm_src[n] = r

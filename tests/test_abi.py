@@ -138,9 +138,13 @@ def test_regroup_workspace_and_arguments():
     f = L.ep_regroup_by_expert
 
     def call(R=16, K=2, H=64, El=4, align=1, cap=64, x=A16, idx=A16, ws=A16,
-             ws_bytes=1 << 20):
-        return f(x, idx, None, R, K, H, El, align, cap, A16, A16, None, A16, A16, A16, ws,
-                 ws_bytes, None)
+             ws_bytes=1 << 20, grp=None, G=1):
+        return f(x, idx, None, grp, G, R, K, H, El, align, cap, A16, A16, None, A16, A16, A16,
+                 ws, ws_bytes, None)
+    assert call(G=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(G=2) == _lib.EP_ERR_INVALID_ARG                 # groups need row_group
+    assert call(G=2, grp=ODD) == _lib.EP_ERR_INVALID_ARG
+    assert call(G=300, grp=A16) == _lib.EP_ERR_UNSUPPORTED      # 1200 bins
     assert call(align=0) == _lib.EP_ERR_INVALID_ARG
     assert call(El=0) == _lib.EP_ERR_INVALID_ARG
     assert call(cap=-1) == _lib.EP_ERR_INVALID_ARG

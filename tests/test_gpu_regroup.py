@@ -107,3 +107,26 @@ def test_regroup_workspace_reused():
         _check(rx, ridx, rw, El, align, workspace=ws)
     hdr = ws[:16].view(torch.int32).cpu().numpy()
     assert hdr[0] == 0 and hdr[3] == 0 and hdr[2] == 3
+
+
+@pytest.mark.parametrize("name,T,H,align", [("skewed_t16384", 3000, 256, 16),
+                                            ("uniform_t4096", 2000, 512, 128)])
+def test_regroup_all_destination_segments_at_once(name, T, H, align):
+    """row_group = send_rank: every destination's received rows regrouped in
+    one call, against the oracle's regroup with the same groups."""
+    s = spec(name, T=T, H=H)
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, s.P, s.E_local)
+    rx, ridx = x[sti], sidx.astype(np.int32)
+    ox, osrc, ow, ocnt, ooff, omap = O.regroup_by_expert(rx, ridx, sw, s.E_local, align,
+                                                         row_group=srk, num_groups=s.P)
+    out = ep.ep_regroup_by_expert(to_dev(rx), to_dev(ridx), to_dev(sw), s.E_local, align,
+                                  row_group=to_dev(srk.astype(np.int32)), num_groups=s.P)
+    M = int(ooff[-1])
+    assert np.array_equal(host(out.tokens_per_expert), ocnt)
+    assert np.array_equal(host(out.expert_offsets), ooff)
+    assert np.array_equal(host(out.row_map), omap)
+    assert np.array_equal(host(out.perm_src)[:M], osrc)
+    assert np.array_equal(host(out.perm_w)[:M].view(np.uint32), ow.view(np.uint32))
+    assert np.array_equal(bits(out.perm_x)[:M], ox)

@@ -49,6 +49,7 @@ ROUTING_PINS = [
 ]
 REGROUP_PINS = [
     pin(RT, "test_regroup_equals_stable_sort_and_bincount", 4),
+    pin(RT, "test_regroup_groups_are_segments_end_to_end"),
     pin(RT, "test_regroup_brute_force_tiny"),
     pin(RT, "test_regroup_restore_is_weighted_sum"),
 ]
@@ -136,14 +137,19 @@ MUTANTS = {
         "    padded = [-(-int(c) // A) * A for c in counts]",
         "    padded = [int(c) for c in counts]", REGROUP_PINS),
     "regroup_rows_descending": (
-        "        rows = [r for r in range(R) if (idx[r] == e).any()]",
-        "        rows = [r for r in range(R - 1, -1, -1) if (idx[r] == e).any()]", REGROUP_PINS),
+        "        rows = [r for r in range(R) if grp[r] == g and (idx[r] == e).any()]",
+        "        rows = [r for r in range(R - 1, -1, -1) if grp[r] == g and (idx[r] == e).any()]",
+        REGROUP_PINS),
+    "regroup_groups_ignored": (
+        "        rows = [r for r in range(R) if grp[r] == g and (idx[r] == e).any()]",
+        "        rows = [r for r in range(R) if (idx[r] == e).any()] if g == 0 else []",
+        REGROUP_PINS),
     "regroup_weight_of_first_slot_wrong": (
         "            perm_w[n] = w[r, k]",
         "            perm_w[n] = w[r, 0]", REGROUP_PINS),
     "regroup_offset_off_by_one": (
-        "            n = offsets[e] + s",
-        "            n = offsets[e] + s + (1 if e else 0)", REGROUP_PINS),
+        "            n = offsets[b] + s",
+        "            n = offsets[b] + s + (1 if b else 0)", REGROUP_PINS),
     "partials_duplicates_counted": (
         "            if r < 0 or r in seen:",
         "            if r < 0:", PARTIAL_PINS),

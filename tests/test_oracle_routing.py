@@ -370,3 +370,29 @@ def test_regroup_rejects_bad_ids_and_alignment():
         O.regroup_by_expert(np.zeros((1, 8), np.uint16), np.array([[1, 1]]), np.ones((1, 2)), 3)
     with pytest.raises(ValueError):
         O.regroup_by_expert(np.zeros((1, 8), np.uint16), np.array([[1]]), np.ones((1, 1)), 3, 0)
+
+
+def test_regroup_groups_are_segments_end_to_end():
+    # every destination's segment regrouped at once (row_group = send_rank)
+    # equals the per-segment regroups laid end to end
+    s = spec("uniform_t4096", T=300, H=8)
+    idx, w = make_routing(s)
+    rng = np.random.default_rng(2)
+    x = rng.integers(0, 1 << 16, size=(s.T, s.H), dtype=np.uint16)
+    sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, s.P, s.E_local)
+    A = 4
+    px, src, pw, cnt, off, rmap = O.regroup_by_expert(x[sti], sidx, sw, s.E_local, A,
+                                                      row_group=srk, num_groups=s.P)
+    base = 0
+    for p in range(s.P):
+        seg = np.flatnonzero(srk == p)
+        qx, qs, qw, qc, qo, qm = O.regroup_by_expert(x[sti[seg]], sidx[seg], sw[seg],
+                                                     s.E_local, A)
+        assert np.array_equal(cnt[p * s.E_local:(p + 1) * s.E_local], qc)
+        assert np.array_equal(off[p * s.E_local:(p + 1) * s.E_local + 1], qo + base)
+        M = int(qo[-1])
+        assert np.array_equal(px[base:base + M], qx)
+        assert np.array_equal(src[base:base + M], np.where(qs >= 0, seg[qs], -1))
+        assert np.array_equal(rmap[seg], np.where(qm >= 0, qm + base, -1))
+        base += M
+    assert base == len(src)
