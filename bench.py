@@ -142,6 +142,83 @@ def build_send_step(torch, ep, s, d_idx, d_w, d_x):
     return step, kb, info
 
 
+def bytes_regroup(H, N, K, M, M_data, B):
+    # ids, weights and row groups of the N received rows; row_map, the source
+    # and weight of every regrouped row, counts and offsets; rows: each
+    # received row read once, every regrouped row (padding included) written
+    return (4 + 4) * N * K + 4 * N + 4 * N * K + 8 * M + 4 * (2 * B + 1) + 2 * H * N + 2 * H * M
+
+
+def build_expert_major_step(torch, ep, s, d_idx, d_w, d_x):
+    """Dispatch, then every destination's received rows regrouped by local
+    expert (aligned), an identity expert, the weighted restore onto the send
+    rows, and the unweighted combine of the per-destination partials.  The
+    receivers' row count N is known on the host, as after a count exchange
+    (routing is fixed, so it is taken once in the setup)."""
+    T, K, P, El, H, A = s.T, s.K, s.P, s.E_local, s.H, s.align
+    cap = T * min(K, P)
+    B = P * El
+    cap_m = T * K + B * (A - 1)        # one row per routed slot, plus padding
+    dev = d_x.device
+    counts, lay = ep.ep_dispatch_layout(d_idx, d_w, P, El, cap)
+    torch.cuda.synchronize()
+    N = int(counts.send_counts.sum().item())
+    send_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    y_send = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    reg = ep.Regrouped(
+        perm_x=torch.empty((cap_m, H), dtype=torch.bfloat16, device=dev),
+        perm_src=torch.empty(cap_m, dtype=torch.int32, device=dev),
+        perm_w=torch.empty(cap_m, dtype=torch.float32, device=dev),
+        tokens_per_expert=torch.empty(B, dtype=torch.int32, device=dev),
+        expert_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev),
+        row_map=torch.empty((N, K), dtype=torch.int32, device=dev))
+    ws = ep.workspace_for(ep.ep_dispatch_layout_workspace_bytes(T, P, El), dev, kind="fused")
+    ws_r = ep.workspace_for(ep.ep_regroup_workspace_bytes(N, B), dev, kind="regroup")
+    recv_x, recv_idx, recv_w, recv_rank = send_x[:N], lay.send_idx[:N], lay.send_w[:N], \
+        lay.send_rank[:N]
+
+    def step(timer=None):
+        st = torch.cuda.current_stream()
+        tk = timer.start("dispatch_layout", st) if timer else None
+        ep.ep_dispatch_layout(d_idx, d_w, P, El, cap, counts=counts, out=lay, workspace=ws)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("permute", st)
+        ep.ep_dispatch_permute(d_x, lay.token_row, cap, out=send_x)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("regroup", st)
+        ep.ep_regroup_by_expert(recv_x, recv_idx, recv_w, El, A, cap_m, row_group=recv_rank,
+                                num_groups=P, out=reg, workspace=ws_r)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("restore", st)
+        ep.ep_combine(reg.perm_x, reg.row_map, recv_w, out=y_send)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("combine", st)
+        ep.ep_combine(y_send, lay.token_row, None, out=out)
+        if timer:
+            timer.stop(tk)
+
+    step()
+    torch.cuda.synchronize()
+    U = int(((d_idx >= 0).any(dim=1)).sum().item())
+    M = int(reg.expert_offsets[-1].item())
+    M_data = int(reg.tokens_per_expert.sum().item())
+    kb = {
+        "dispatch_layout": bytes_dispatch_layout(T, K, P, s.E, N),
+        "permute": bytes_permute(H, U, N),
+        "regroup": bytes_regroup(H, N, K, M, M_data, B),
+        "restore": 2 * H * M_data + 8 * N * K + 2 * H * N,
+        "combine": 2 * H * N + 4 * T * K + 2 * H * T,
+    }
+    info = {"num_send": N, "routed_tokens": U, "capacity": cap, "regrouped_rows": M,
+            "regrouped_data_rows": M_data, "align": A}
+    return step, kb, info
+
+
 def build_batched_step(torch, ep, s, d_idx, d_w, d_x):
     T, K, El, H, M = s.T, s.K, s.E_local, s.H, s.max_num_tokens
     first = s.first_expert
@@ -283,7 +360,21 @@ def cpu_baseline(s, budget_tokens):
     x = make_hidden(sub)
     T, K, H = sub.T, sub.K, sub.H
     t0 = time.perf_counter()
-    if s.layout == "batched":
+    if s.layout == "expert_major":
+        El, P, A = s.E_local, s.P, s.align
+        sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, P, El)
+        N = len(sti)
+        sx = O.dispatch_permute(x, sti)
+        px, src, pw, cnt, off, rmap = O.regroup_by_expert(sx, sidx, sw, El, A, row_group=srk,
+                                                          num_groups=P)
+        y = O.combine(px, rmap, sw)
+        O.combine_partials(y, trow)
+        U = int((idx >= 0).any(axis=1).sum())
+        M, Md = int(off[-1]), int(cnt.sum())
+        nbytes = (bytes_dispatch_layout(T, K, P, s.E, N) + bytes_permute(H, U, N) +
+                  bytes_regroup(H, N, K, M, Md, P * El) + 2 * H * Md + 8 * N * K + 2 * H * N +
+                  2 * H * N + 4 * T * K + 2 * H * T)
+    elif s.layout == "batched":
         bx, tpe, trow = O.batched_prepare(x, idx, s.first_expert, s.E_local, s.max_num_tokens)
         O.combine(bx.reshape(-1, H), trow, w)
         U_local = int(((idx >= s.first_expert) & (idx < s.first_expert + s.E_local))
@@ -411,6 +502,8 @@ def main():
 
     if s.layout == "batched":
         step, kbytes, info = build_batched_step(torch, ep, s, d_idx, d_w, d_x)
+    elif s.layout == "expert_major":
+        step, kbytes, info = build_expert_major_step(torch, ep, s, d_idx, d_w, d_x)
     elif s.fp8:
         step, kbytes, info = build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x)
     else:
@@ -469,7 +562,8 @@ def main():
     torch.cuda.synchronize()
     kern_us = timer.averages_us()
     per_launch = info.get("per_launch_bytes", kbytes)
-    dom = max((k for k in kern_us if k not in ("counts", "layout", "dispatch_layout")),
+    dom = max((k for k in kern_us if k not in ("counts", "layout", "dispatch_layout",
+                                                   "regroup")),
               key=lambda k: kern_us[k])
     dom_gbs = per_launch[dom] / (kern_us[dom] * 1e-6) / 1e9
     trec = traffic_from_profiles(s.name, dom, kernel_source_digest())
@@ -522,7 +616,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or {"skewed_t16384": 6144, "uniform_t4096": 4096, "tiny": 256,
-                                "batched_t8192": 8192, "fp8_t32768": 3072}.get(s.name, 1024)
+                                "batched_t8192": 8192, "fp8_t32768": 3072,
+                                "expert_major_t16384": 384}.get(s.name, 1024)
         log(f"[bench] timing the CPU oracle on {n} tokens")
         result["cpu_baseline"] = cpu_baseline(s, n)
     print(json.dumps(result), flush=True)

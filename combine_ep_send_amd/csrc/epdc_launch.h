@@ -148,6 +148,8 @@ hipError_t launch_zero_pad(const PadArgs& a, hipStream_t s);
 constexpr int kMaxRowBlock = 1024;
 // Workgroup of the bf16 permute (one 16-byte piece per thread).
 constexpr int kPermuteBlock = 128;
+// Workgroup of the combine for sparse slots (several pieces per thread).
+constexpr int kSparseBlock = 128;
 
 struct CombineArgs {
   const void* y;

@@ -318,6 +318,82 @@ __global__ __launch_bounds__(kMaxRowBlock) void combine_kernel(CombineArgs a, in
   st_stream(static_cast<u32x4*>(a.out) + t * H8 + j, o);
 }
 
+// ---------------------------------------------------------------------------
+// Combine for sparse slots (most tokens name one or two rows, e.g. expert
+// outputs restored onto received rows): the same sums in the same order, but
+// a thread owns PER pieces and each valid slot's row is loaded and added in
+// turn, so every wave keeps PER loads in flight instead of one.
+// ---------------------------------------------------------------------------
+template <int KMAX, bool WEIGHTED, int PER>
+__global__ __launch_bounds__(kSparseBlock) void combine_sparse_kernel(CombineArgs a, int nchunks,
+                                                                      int64_t item0) {
+#pragma clang fp contract(off)
+  const int H8 = a.H >> 3;
+  const int64_t item = item0 + blockIdx.x;
+  const int64_t t = udiv(item, nchunks);
+  const int j0 = int(item - t * nchunks) * (kSparseBlock * PER) + int(threadIdx.x);
+  int32_t rows[KMAX];
+  float wk[KMAX];
+  load_slots<KMAX>(a.token_row, t, a.K, rows);
+  if (WEIGHTED) load_slots<KMAX>(a.w, t, a.K, wk);
+  bool use[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    use[k] = k < a.K && rows[k] >= 0 && int64_t(rows[k]) < a.R;
+    if (!WEIGHTED) {         // unweighted: each distinct row once
+#pragma unroll
+      for (int q = 0; q < k; ++q)
+        if (use[q] && rows[q] == rows[k]) use[k] = false;
+    }
+  }
+  const u32x4* y = static_cast<const u32x4*>(a.y);
+  float acc[PER][8];
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (!use[k]) continue;
+    u32x4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = j0 + i * kSparseBlock;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (j < H8) v[i] = ld_stream(y + int64_t(rows[k]) * H8 + j);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (WEIGHTED) {
+        const float wt = wk[k];
+        const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float p0 = wt * bf16_lo(wd[q]);
+          const float p1 = wt * bf16_hi(wd[q]);
+          acc[i][2 * q] = acc[i][2 * q] + p0;
+          acc[i][2 * q + 1] = acc[i][2 * q + 1] + p1;
+        }
+      } else {
+        add_row(acc[i], v[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = j0 + i * kSparseBlock;
+    if (j >= H8) continue;
+    if (a.bias0) add_row(acc[i], ld_stream(static_cast<const u32x4*>(a.bias0) + t * H8 + j));
+    if (a.bias1) add_row(acc[i], ld_stream(static_cast<const u32x4*>(a.bias1) + t * H8 + j));
+    u32x4 o;
+    o.x = f32_to_bf16_rne(acc[i][0]) | (f32_to_bf16_rne(acc[i][1]) << 16);
+    o.y = f32_to_bf16_rne(acc[i][2]) | (f32_to_bf16_rne(acc[i][3]) << 16);
+    o.z = f32_to_bf16_rne(acc[i][4]) | (f32_to_bf16_rne(acc[i][5]) << 16);
+    o.w = f32_to_bf16_rne(acc[i][6]) | (f32_to_bf16_rne(acc[i][7]) << 16);
+    st_stream(static_cast<u32x4*>(a.out) + t * H8 + j, o);
+  }
+}
+
 // ---- launch shapes -----------------------------------------------------------
 
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
@@ -376,9 +452,34 @@ void launch_permute_fp8_k(const RowArgs& a, hipStream_t s) {
 
 template <int KMAX>
 void launch_combine_k(const CombineArgs& a, hipStream_t s) {
+  const int64_t H8 = a.H >> 3;
+  if (a.R < 2 * a.T) {
+    // Fewer than two rows per token on average: the sparse form, up to 7
+    // pieces per thread (a 7168-channel row in one workgroup).
+    const int per = int((H8 + kSparseBlock - 1) / kSparseBlock) < 7
+                        ? int((H8 + kSparseBlock - 1) / kSparseBlock) : 7;
+    const int64_t nch = (H8 + int64_t(kSparseBlock) * per - 1) / (int64_t(kSparseBlock) * per);
+    for_each_launch(a.T * nch, [&](int64_t i0, unsigned g) {
+#define EPDC_SPARSE(P)                                                                    \
+  if (a.w)                                                                                \
+    combine_sparse_kernel<KMAX, true, P><<<g, kSparseBlock, 0, s>>>(a, int(nch), i0);    \
+  else                                                                                    \
+    combine_sparse_kernel<KMAX, false, P><<<g, kSparseBlock, 0, s>>>(a, int(nch), i0);
+      switch (per) {
+        case 1: EPDC_SPARSE(1) break;
+        case 2: EPDC_SPARSE(2) break;
+        case 3: EPDC_SPARSE(3) break;
+        case 4: EPDC_SPARSE(4) break;
+        case 5: EPDC_SPARSE(5) break;
+        case 6: EPDC_SPARSE(6) break;
+        default: EPDC_SPARSE(7) break;
+      }
+#undef EPDC_SPARSE
+    });
+    return;
+  }
   // One piece per thread; a workgroup covers the whole row when it has at
   // most kMaxRowBlock pieces (rounded up to whole waves), else equal chunks.
-  const int64_t H8 = a.H >> 3;
   const int64_t nch = (H8 + kMaxRowBlock - 1) / kMaxRowBlock;
   const int64_t per_chunk = (H8 + nch - 1) / nch;
   const int threads = int((per_chunk + kWave - 1) / kWave) * kWave;

@@ -48,10 +48,11 @@ class WorkloadSpec:
     routing: str = "uniform"    # "uniform" | "zipf"
     zipf_s: float = 1.2
     unrouted_frac: float = 0.0  # fraction of slots forced to -1
-    layout: str = "send"        # "send" (destination-major) | "batched"
+    layout: str = "send"        # "send" (destination-major) | "batched" | "expert_major"
     first_expert: int = 0       # batched layout: first local expert
     max_num_tokens: int = 0     # batched layout: rows per local expert
     fp8: bool = False           # quantise rows to e4m3 on dispatch
+    align: int = 1              # expert-major layout: rows per expert padded to a multiple
     chunks: int = 1             # contiguous token chunks
     streams: int = 1            # HIP streams the chunks alternate over
     seed: int = 0
@@ -74,6 +75,9 @@ CONFIGS = {
     "skewed_t16384": WorkloadSpec(
         "skewed_t16384", T=16384, H=7168, E=256, K=8, P=32, routing="zipf",
         zipf_s=1.2, unrouted_frac=0.05),
+    "expert_major_t16384": WorkloadSpec(
+        "expert_major_t16384", T=16384, H=7168, E=256, K=8, P=32, routing="zipf",
+        zipf_s=1.2, unrouted_frac=0.05, layout="expert_major", align=128),
     "fp8_t32768": WorkloadSpec(
         "fp8_t32768", T=32768, H=7168, E=256, K=8, P=32, fp8=True, chunks=4,
         streams=2),
