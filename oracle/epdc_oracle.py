@@ -438,7 +438,8 @@ def combine_partials(y_bits, token_row, biases=()):
     """[axolotl] module overview and combine: the local expert kernel already
     weights and sums over its slots, and combine sums the per-destination
     partial outputs back onto the source tokens, without weights ([uccl]
-    Buffer.combine without topk_weights: "addition without weights").
+    Buffer.combine, when no topk_weights are given, adds the rows as they
+    are).
 
     Each distinct row of token t (the send row of one destination; slots
     owned by the same destination share it) is added once, in the order of
