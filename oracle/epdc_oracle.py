@@ -31,7 +31,10 @@ rounded then sum rounded, k ascending, starting from +0.0, rounded once to
 bf16 (nearest, ties to even); fp8 is OCP E4M3 (``float8_e4m3fn``) with
 ``scale = amax / 448`` in float32, the quotient ``x / scale`` rounded to
 float32 and then to the nearest e4m3 value (ties to even), saturating at 448,
-and an all-zero group giving scale 0 and code 0x00.
+and an all-zero group giving scale 0 and code 0x00; a power-of-two scale is
+the smallest power of two at or above amax / 448, its UE8M0 byte is the
+exponent plus 127 (at least 0, i.e. 2^-127), and four such bytes pack into an
+int32 with the lowest group in the lowest byte.
 
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against brute force, closed forms, library routines (numpy sorts and
@@ -53,19 +56,30 @@ __all__ = [
     "f32_to_bf16",
     "e4m3_decode",
     "e4m3_encode",
+    "round_scale_pow2",
+    "ue8m0_encode",
+    "ue8m0_decode",
+    "pack_ue8m0",
+    "unpack_ue8m0",
     "quantize_rows_fp8",
     "dequantize_rows_fp8",
     "dispatch_permute_fp8",
     "batched_prepare",
+    "batched_prepare_fp8",
+    "scale_storage",
     "regroup_by_expert",
     "combine",
     "combine_partials",
     "FP8_MAX",
     "FP8_GROUP",
+    "UE8M0_BIAS",
+    "SCALE_FORMATS",
 ]
 
 FP8_MAX = 448.0   # largest finite OCP E4M3 magnitude (S.1111.110)
 FP8_GROUP = 128   # channels per fp32 scale ([uccl] Buffer.dispatch)
+UE8M0_BIAS = 127  # UE8M0: 8 exponent bits, no sign, no mantissa
+SCALE_FORMATS = ("f32", "pow2", "ue8m0")
 
 
 # --------------------------------------------------------------------------
@@ -245,15 +259,71 @@ def e4m3_encode(values):
     return (code | (sign << 7)).astype(np.uint8)
 
 
-def quantize_rows_fp8(x_bits):
-    """[uccl] Buffer.dispatch / low_latency_dispatch fp8 input: e4m3 rows plus
-    one float32 scale per token per 128 channels.
+def round_scale_pow2(s):
+    """[uccl] Buffer.low_latency_dispatch ``round_scale``: the scale becomes a
+    power of two.  Reading: the smallest power of two that is >= s, so that
+    x / scale still lies within the e4m3 range; 0 stays 0.  Input and output
+    float32 (every such power of two from 2^-149 up is a float32)."""
+    s64 = np.asarray(s, dtype=np.float32).astype(np.float64)
+    m, e = np.frexp(s64)                    # s = m * 2^e with 0.5 <= m < 1
+    p = np.where(m == 0.5, s64, np.ldexp(1.0, e))
+    return np.where(s64 == 0.0, 0.0, p).astype(np.float32)
 
-    For each group of 128 channels: amax = max |x| (exact), scale =
-    fl32(amax / 448), q = e4m3(fl32(x / scale)).  A group whose amax is 0
-    gets scale 0.0 and all codes 0x00.  Returns (uint8 [R,H], float32
-    [R, H/128]).
+
+def ue8m0_encode(p):
+    """UE8M0 byte of a power of two p ([uccl] Buffer.low_latency_dispatch
+    ``use_ue8m0``): 8 exponent bits with bias 127, no sign and no mantissa,
+    so 2^e is stored as e + 127.  Powers below 2^-127, and 0, take the
+    smallest code 0x00 (2^-127): a larger scale than asked for, which keeps
+    x / scale in range.  The largest scale a finite bf16 group can ask for
+    is 2^120 (code 247), so no group reaches the top codes."""
+    p64 = np.asarray(p, dtype=np.float32).astype(np.float64)
+    e = np.frexp(p64)[1] - 1                # p = 2^e
+    b = np.where(p64 > 0, np.clip(e + UE8M0_BIAS, 0, 254), 0)
+    return b.astype(np.uint8)
+
+
+def ue8m0_decode(b):
+    """float32 value 2^(b - 127) of UE8M0 bytes 0..254."""
+    b = np.asarray(b, dtype=np.int64)
+    return np.ldexp(1.0, b - UE8M0_BIAS).astype(np.float32)
+
+
+def pack_ue8m0(b):
+    """[uccl] Buffer.low_latency_dispatch: UE8M0 scales packed four to a
+    32-bit int ([.., H/512] int).  Reading: int j holds the bytes of groups
+    4j..4j+3 with group 4j in the least significant byte."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.uint32)
+    *lead, G = b.shape
+    if G % 4:
+        raise ValueError("UE8M0 packing needs a multiple of 4 groups (H % 512 == 0)")
+    b = b.reshape(*lead, G // 4, 4)
+    word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    return word.astype(np.uint32).view(np.int32)
+
+
+def unpack_ue8m0(packed):
+    """Inverse of pack_ue8m0: the group bytes, [.., 4 * words] uint8."""
+    w = np.asarray(packed, dtype=np.int32).view(np.uint32)
+    parts = [(w >> np.uint32(8 * i)) & np.uint32(0xFF) for i in range(4)]
+    return np.stack(parts, axis=-1).reshape(*w.shape[:-1], -1).astype(np.uint8)
+
+
+def quantize_rows_fp8(x_bits, scale_fmt="f32"):
+    """[uccl] Buffer.dispatch / low_latency_dispatch fp8 input: e4m3 rows plus
+    one scale per token per 128 channels.
+
+    For each group of 128 channels: amax = max |x| (exact) and s =
+    fl32(amax / 448).  The scale is s (``f32``), the smallest power of two
+    >= s (``pow2``, [uccl] ``round_scale``), or that power as a UE8M0 byte
+    (``ue8m0``, [uccl] ``use_ue8m0``; the quantizer then divides by the
+    byte's value 2^(b-127)).  q = e4m3(fl32(x / scale)).  A group whose amax
+    is 0 gets all codes 0x00 and scale 0.0 (byte 0x00 in ``ue8m0``).
+    Returns (uint8 [R,H], scales): float32 [R, H/128] for ``f32`` and
+    ``pow2``, int32 [R, H/512] (pack_ue8m0) for ``ue8m0``.
     """
+    if scale_fmt not in SCALE_FORMATS:
+        raise ValueError(f"scale_fmt must be one of {SCALE_FORMATS}")
     x = bf16_to_f32(x_bits)
     R, H = x.shape
     if H % FP8_GROUP:
@@ -261,11 +331,19 @@ def quantize_rows_fp8(x_bits):
     g = x.reshape(R, H // FP8_GROUP, FP8_GROUP)
     amax = np.abs(g).max(axis=2)
     scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    if scale_fmt == "pow2":
+        scale = round_scale_pow2(scale)
+    elif scale_fmt == "ue8m0":
+        byte = ue8m0_encode(round_scale_pow2(scale))
+        scale = np.where(amax > 0, ue8m0_decode(byte), np.float32(0.0)).astype(np.float32)
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
     quot = (g / safe[:, :, None]).astype(np.float32)
     q = e4m3_encode(quot)
     q = np.where((scale > 0)[:, :, None], q, np.uint8(0))
-    return q.reshape(R, H).astype(np.uint8), scale
+    q = q.reshape(R, H).astype(np.uint8)
+    if scale_fmt == "ue8m0":
+        return q, pack_ue8m0(byte)
+    return q, scale
 
 
 def dequantize_rows_fp8(q, scales):
@@ -320,6 +398,51 @@ def batched_prepare(x_bits, topk_idx, first_expert, num_local_experts,
             b_x[e, slot] = x[t]
             token_row[t, hit_slots[t]] = e * M + slot
     return b_x, tokens_per_expert, token_row
+
+
+def batched_prepare_fp8(x_bits, topk_idx, first_expert, num_local_experts,
+                        max_num_tokens, scale_fmt="f32"):
+    """[uccl] Buffer.low_latency_dispatch with ``use_fp8`` (the received
+    tokens per local expert as e4m3 rows [E_local, max, H] plus scales
+    [E_local, max, H/128] float, or packed UE8M0 [E_local, max, H/512] int),
+    and [vllm] BatchedPrepareAndFinalize.prepare, quantized branch (zeroed
+    buffers, each expert's rows quantized per token).
+
+    Quantization is per token and per 128 channels, so the buffer is the
+    expert-batched gather of quantize_rows_fp8(x): slot s of expert e holds
+    the codes and scales of the token batched_prepare puts there.  Padding
+    slots hold codes 0x00 and scale 0 (int 0 in ``ue8m0``).  Returns
+    (b_q uint8 [E_local, max, H], b_scale [E_local, max, H/128] float32 or
+    [E_local, max, H/512] int32, tokens_per_expert, token_row); the scale
+    array is in logical (expert, slot, group) order (scale_storage gives the
+    memory order).
+    """
+    x = np.asarray(x_bits, dtype=np.uint16)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    H = x.shape[1]
+    El, M = int(num_local_experts), int(max_num_tokens)
+    q, sc = quantize_rows_fp8(x, scale_fmt)
+    _, tokens_per_expert, token_row = batched_prepare(x, idx, first_expert, El, M)
+    b_q = np.zeros((El, M, H), dtype=np.uint8)
+    b_scale = np.zeros((El, M, sc.shape[1]), dtype=sc.dtype)
+    for e in range(El):
+        tokens = np.flatnonzero((idx == (first_expert + e)).any(axis=1))
+        for slot, t in enumerate(tokens):
+            b_q[e, slot] = q[t]
+            b_scale[e, slot] = sc[t]
+    return b_q, b_scale, tokens_per_expert, token_row
+
+
+def scale_storage(b_scale, col_major):
+    """Memory order of an expert-batched scale array [E_local, max, G]:
+    row-major, or ([uccl] Buffer.low_latency_dispatch) column-major in the
+    last two dimensions, i.e. each expert's [max, G] block stored as [G, max].
+    Returns the flat array in memory order."""
+    b = np.asarray(b_scale)
+    if col_major:
+        b = b.transpose(0, 2, 1)
+    return np.ascontiguousarray(b).reshape(-1)
 
 
 # --------------------------------------------------------------------------

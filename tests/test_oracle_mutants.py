@@ -15,6 +15,7 @@ import pytest
 
 import tests.test_oracle_numerics as NUM
 import tests.test_oracle_routing as RT
+import tests.test_oracle_scales as SC
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_PATH = os.path.join(os.path.dirname(HERE), "oracle", "epdc_oracle.py")
@@ -72,6 +73,15 @@ FORMAT_PINS = [
     pin(NUM, "test_e4m3_hand_cases", GOLDEN),
     pin(NUM, "test_quantize_hand_row", GOLDEN),
     pin(NUM, "test_quantize_properties"),
+]
+SCALE_PINS = [
+    pin(SC, "test_pow2_is_the_smallest_power_at_or_above"),
+    pin(SC, "test_ue8m0_bytes_match_torch_e8m0_on_powers_of_two"),
+    pin(SC, "test_ue8m0_small_scales_clamp_to_the_lowest_code"),
+    pin(SC, "test_packing_is_a_little_endian_int_view"),
+    pin(SC, "test_scale_formats_hand_worked"),
+    pin(SC, "test_pow2_and_ue8m0_codes_against_torch"),
+    pin(SC, "test_batched_fp8_is_the_gather_of_quantized_rows"),
 ]
 BATCHED_PINS = [
     pin(RT, "test_batched_equals_stable_argsort", 0, 32),
@@ -165,6 +175,28 @@ MUTANTS = {
         "acc = (acc + bf16_to_f32(np.asarray(b, dtype=np.uint16))).astype(np.float32)",
         "acc = (acc - bf16_to_f32(np.asarray(b, dtype=np.uint16))).astype(np.float32)",
         PARTIAL_PINS),
+    "pow2_rounds_down": (
+        "p = np.where(m == 0.5, s64, np.ldexp(1.0, e))",
+        "p = np.where(m == 0.5, s64, np.ldexp(1.0, e - 1))", SCALE_PINS),
+    "pow2_exact_powers_doubled": (
+        "p = np.where(m == 0.5, s64, np.ldexp(1.0, e))",
+        "p = np.ldexp(1.0, e)", SCALE_PINS),
+    "ue8m0_bias_128": ("UE8M0_BIAS = 127", "UE8M0_BIAS = 128", SCALE_PINS),
+    "ue8m0_not_clamped": (
+        "np.clip(e + UE8M0_BIAS, 0, 254)", "(e + UE8M0_BIAS) % 256", SCALE_PINS),
+    "ue8m0_packed_big_endian": (
+        "word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)",
+        "word = b[..., 3] | (b[..., 2] << 8) | (b[..., 1] << 16) | (b[..., 0] << 24)",
+        SCALE_PINS),
+    "ue8m0_quantizes_with_unclamped_power": (
+        "scale = np.where(amax > 0, ue8m0_decode(byte), np.float32(0.0)).astype(np.float32)",
+        "scale = round_scale_pow2(scale)", SCALE_PINS),
+    "batched_fp8_scale_of_next_token": (
+        "            b_scale[e, slot] = sc[t]",
+        "            b_scale[e, slot] = sc[min(t + 1, T - 1)]", SCALE_PINS),
+    "batched_fp8_padding_scale_one": (
+        "    b_scale = np.zeros((El, M, sc.shape[1]), dtype=sc.dtype)",
+        "    b_scale = np.ones((El, M, sc.shape[1]), dtype=sc.dtype)", SCALE_PINS),
     "batched_slots_descending": (
         "tokens = np.flatnonzero(hit_slots.any(axis=1))",
         "tokens = np.flatnonzero(hit_slots.any(axis=1))[::-1]", BATCHED_PINS),
@@ -194,6 +226,6 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 def test_unmutated_copy_passes_all_pins(monkeypatch):
     mod = make_mutant("FP8_GROUP = 128", "FP8_GROUP = 128")
     for module, fn, args in (ROUTING_PINS + COMBINE_PINS + FORMAT_PINS + BATCHED_PINS +
-                             PARTIAL_PINS + REGROUP_PINS):
+                             PARTIAL_PINS + REGROUP_PINS + SCALE_PINS):
         monkeypatch.setattr(module, "O", mod)
         getattr(module, fn)(*args)
