@@ -79,6 +79,13 @@ def bytes_batched(H, T, K, El, M, U_local):
     return 2 * H * U_local + 8 * T * K + 2 * H * El * M + 4 * El + 4 * T * K
 
 
+def bytes_batched_fp8(H, T, K, El, M, U_local, units):
+    # bf16 rows of the local tokens and the ids in; e4m3 rows, one 32-bit
+    # scale word per unit (128 channels, or 512 with UE8M0), counts and
+    # token_row out, padding included
+    return 2 * H * U_local + 8 * T * K + H * El * M + 4 * units * El * M + 4 * El + 4 * T * K
+
+
 # ---------------------------------------------------------------------------
 
 class Timer:
@@ -253,6 +260,62 @@ def build_batched_step(torch, ep, s, d_idx, d_w, d_x):
     return step, kb, {"rows": rows, "local_tokens": U_local}
 
 
+def dequantize_batched(torch, q, sc, scale_fmt):
+    """bf16 fl32(decode(q) * scale) of an fp8 batched buffer: the output of an
+    identity expert behind fp8, the combine's input (built outside the timed
+    region)."""
+    El, M, H = q.shape
+    if scale_fmt == "ue8m0":
+        b = sc.contiguous().view(torch.uint8).to(torch.int32)        # [El, M, H/128] bytes
+        scale = torch.ldexp(torch.ones_like(b, dtype=torch.float32), b - 127)
+    else:
+        scale = sc.contiguous()
+    vals = q.float().view(El, M, H // 128, 128) * scale[..., None]
+    return vals.view(El, M, H).to(torch.bfloat16)
+
+
+def build_batched_fp8_step(torch, ep, s, d_idx, d_w, d_x):
+    T, K, El, H, M = s.T, s.K, s.E_local, s.H, s.max_num_tokens
+    first, fmt, colm = s.first_expert, s.scale_fmt, s.scale_col_major
+    dev = d_x.device
+    b_q = torch.empty((El, M, H), dtype=torch.float8_e4m3fn, device=dev)
+    b_s = ep.batched_scale_like(El, M, H, fmt, colm, dev)
+    tpe = torch.empty(El, dtype=torch.int32, device=dev)
+    trow = torch.empty((T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = ep.workspace_for(ep.ep_batched_workspace_bytes(T, El, M), dev)
+    ep.ep_batched_prepare_fp8(d_x, d_idx, first, El, M, scale_fmt=fmt, scale_col_major=colm,
+                              out=b_q, out_scale=b_s, tokens_per_expert=tpe, token_row=trow,
+                              workspace=ws)
+    y = dequantize_batched(torch, b_q, b_s, fmt)
+
+    def step(timer=None):
+        st = torch.cuda.current_stream()
+        tk = timer.start("batched_prepare_fp8", st) if timer else None
+        ep.ep_batched_prepare_fp8(d_x, d_idx, first, El, M, scale_fmt=fmt,
+                                  scale_col_major=colm, out=b_q, out_scale=b_s,
+                                  tokens_per_expert=tpe, token_row=trow, workspace=ws)
+        if timer:
+            timer.stop(tk)
+            tk = timer.start("combine", st)
+        ep.ep_combine(y, trow, d_w, out=out)
+        if timer:
+            timer.stop(tk)
+
+    step()
+    torch.cuda.synchronize()
+    local = (d_idx >= first) & (d_idx < first + El)
+    U_local = int(local.any(dim=1).sum().item())
+    rows = int(tpe.sum().item())
+    units = H // (512 if fmt == "ue8m0" else 128)
+    kb = {
+        "batched_prepare_fp8": bytes_batched_fp8(H, T, K, El, M, U_local, units),
+        "combine": bytes_combine(H, T, K, rows),
+    }
+    return step, kb, {"rows": rows, "local_tokens": U_local, "scale_fmt": fmt,
+                      "scale_col_major": colm}
+
+
 def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, s.chunks
     dev = d_x.device
@@ -374,6 +437,25 @@ def cpu_baseline(s, budget_tokens):
         nbytes = (bytes_dispatch_layout(T, K, P, s.E, N) + bytes_permute(H, U, N) +
                   bytes_regroup(H, N, K, M, Md, P * El) + 2 * H * Md + 8 * N * K + 2 * H * N +
                   2 * H * N + 4 * T * K + 2 * H * T)
+    elif s.layout == "batched" and s.fp8:
+        # max_num_tokens scaled with the sample, so padding keeps its share
+        El, M = s.E_local, -(-s.max_num_tokens * T // s.T)
+        bq, bs, tpe, trow = O.batched_prepare_fp8(x, idx, s.first_expert, El, M, s.scale_fmt)
+        # the identity expert behind fp8 (untimed, as on the GPU): the used rows dequantized
+        t_prep = time.perf_counter()
+        used, local = np.unique(trow[trow >= 0], return_inverse=True)
+        lrow = np.full(trow.shape, -1, dtype=np.int32)
+        lrow[trow >= 0] = local
+        scales = bs.reshape(El * M, -1)[used]
+        if s.scale_fmt == "ue8m0":
+            scales = O.ue8m0_decode(O.unpack_ue8m0(scales))
+        y = O.dequantize_rows_fp8(bq.reshape(El * M, H)[used], scales)
+        t0 += time.perf_counter() - t_prep
+        O.combine(y, lrow, w)
+        U_local = int(((idx >= s.first_expert) & (idx < s.first_expert + El)).any(axis=1).sum())
+        units = H // (512 if s.scale_fmt == "ue8m0" else 128)
+        nbytes = bytes_batched_fp8(H, T, K, El, M, U_local, units) + \
+            bytes_combine(H, T, K, int(tpe.sum()))
     elif s.layout == "batched":
         bx, tpe, trow = O.batched_prepare(x, idx, s.first_expert, s.E_local, s.max_num_tokens)
         O.combine(bx.reshape(-1, H), trow, w)
@@ -413,7 +495,9 @@ def cpu_baseline(s, budget_tokens):
         "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"first {T} tokens of the {s.name} workload (same generator and seed), "
-                  f"all phases, numpy single-threaded",
+                  f"all phases, numpy single-threaded" +
+                  (f", max_num_tokens scaled to {-(-s.max_num_tokens * T // s.T)}"
+                   if s.layout == "batched" and s.fp8 else ""),
     }
 
 
@@ -500,7 +584,9 @@ def main():
     d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
     del x
 
-    if s.layout == "batched":
+    if s.layout == "batched" and s.fp8:
+        step, kbytes, info = build_batched_fp8_step(torch, ep, s, d_idx, d_w, d_x)
+    elif s.layout == "batched":
         step, kbytes, info = build_batched_step(torch, ep, s, d_idx, d_w, d_x)
     elif s.layout == "expert_major":
         step, kbytes, info = build_expert_major_step(torch, ep, s, d_idx, d_w, d_x)
@@ -617,6 +703,7 @@ def main():
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or {"skewed_t16384": 6144, "uniform_t4096": 4096, "tiny": 256,
                                 "batched_t8192": 8192, "fp8_t32768": 3072,
+                                "batched_fp8_t8192": 4096,
                                 "expert_major_t16384": 384}.get(s.name, 1024)
         log(f"[bench] timing the CPU oracle on {n} tokens")
         result["cpu_baseline"] = cpu_baseline(s, n)

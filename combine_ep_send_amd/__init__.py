@@ -29,6 +29,8 @@ from .ops import (  # noqa: F401
     Regrouped,
     SendLayout,
     ep_batched_prepare,
+    ep_batched_prepare_fp8,
+    batched_scale_like,
     ep_batched_workspace_bytes,
     ep_build_send_layout,
     ep_combine,

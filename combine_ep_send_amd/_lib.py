@@ -17,6 +17,9 @@ EP_ERR_WORKSPACE = -3
 EP_ERR_LAUNCH = -4
 EP_DTYPE_BF16 = 0
 EP_DTYPE_FP8_E4M3 = 1
+EP_SCALE_F32 = 0
+EP_SCALE_POW2 = 1
+EP_SCALE_UE8M0 = 2
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -44,6 +47,9 @@ _SIGNATURES = {
     "ep_dispatch_permute": (_I32, [_P, _I64, _I32, _P, _I32, _I64, _I32, _P, _P, _P]),
     "ep_batched_prepare": (
         _I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "ep_batched_prepare_fp8": (
+        _I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
+               _P]),
     "ep_combine": (_I32, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _P, _P]),
 }
 

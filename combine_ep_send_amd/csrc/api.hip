@@ -361,6 +361,8 @@ int ep_dispatch_permute(const void* x, int64_t num_tokens, int hidden, const int
   a.capacity = num_send_capacity;
   a.out = send_x;
   a.out_scale = fp8 ? send_scale : nullptr;
+  a.scale_fmt = kScaleF32;
+  a.scale_block_rows = 0;
   return launch_status(fp8 ? launch_permute_fp8(a, stream) : launch_permute_bf16(a, stream));
 }
 
@@ -405,7 +407,7 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_token
   z.tokens_per_expert = tokens_per_expert;
   z.E_local = num_local_experts;
   z.max_tokens = max_num_tokens;
-  z.H = hidden;
+  z.row_pieces = hidden >> 3;
   z.b_x = b_x;
   if (launch_zero_pad(z, stream) != hipSuccess) return EP_ERR_LAUNCH;
 
@@ -420,6 +422,82 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_token
   r.out_scale = nullptr;
   r.sparse = true;
   return launch_status(launch_permute_bf16(r, stream));
+}
+
+int ep_batched_prepare_fp8(const void* x, const int64_t* topk_idx, int64_t num_tokens,
+                           int num_topk, int hidden, int first_expert, int num_local_experts,
+                           int64_t max_num_tokens, int scale_fmt, int scale_col_major,
+                           void* b_q, void* b_scale, int32_t* tokens_per_expert,
+                           int32_t* token_row, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (num_tokens < 0 || num_topk < 1 || num_local_experts < 1 || max_num_tokens < 0 ||
+      first_expert < 0)
+    return EP_ERR_INVALID_ARG;
+  if (scale_fmt != EP_SCALE_F32 && scale_fmt != EP_SCALE_POW2 && scale_fmt != EP_SCALE_UE8M0)
+    return EP_ERR_INVALID_ARG;
+  if (scale_col_major != 0 && scale_col_major != 1) return EP_ERR_INVALID_ARG;
+  if (num_tokens >= kMaxTokens || num_topk > EPDC_MAX_TOPK ||
+      num_local_experts > EPDC_MAX_BINS || num_tokens * num_topk > INT32_MAX)
+    return EP_ERR_UNSUPPORTED;
+  if (int64_t(num_local_experts) * max_num_tokens > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  int st = check_hidden(hidden, true);
+  if (st != EP_OK) return st;
+  const bool ue8m0 = scale_fmt == EP_SCALE_UE8M0;
+  if (ue8m0 && hidden % (4 * EPDC_FP8_GROUP) != 0) return EP_ERR_INVALID_ARG;
+  const int units = ue8m0 ? hidden / (4 * EPDC_FP8_GROUP) : hidden / EPDC_FP8_GROUP;
+  if (!arr_ok(x, num_tokens, 16) || !arr_ok(topk_idx, num_tokens, 8) ||
+      !arr_ok(token_row, num_tokens, 4) || !arr_ok(b_q, max_num_tokens, 16) ||
+      !arr_ok(b_scale, max_num_tokens, 4) || !arr_ok(tokens_per_expert, 1, 4))
+    return EP_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < ep_batched_workspace_bytes(num_tokens, num_local_experts, max_num_tokens))
+    return EP_ERR_WORKSPACE;
+
+  // 1. scan: counts, slots and token_row; 2. zero codes and scales past each
+  // count; 3. the token-major fp8 permute writes the data rows and scales.
+  ScanArgs a{};
+  a.topk_idx = topk_idx;
+  a.T = num_tokens;
+  a.K = num_topk;
+  a.bins = num_local_experts;
+  a.ctrl = static_cast<uint32_t*>(workspace);
+  a.status = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
+  a.token_row = token_row;
+  a.first_expert = first_expert;
+  a.max_tokens = max_num_tokens;
+  a.tokens_per_expert = tokens_per_expert;
+  if (launch_batched_scan(a, stream) != hipSuccess) return EP_ERR_LAUNCH;
+
+  PadArgs z{};
+  z.tokens_per_expert = tokens_per_expert;
+  z.E_local = num_local_experts;
+  z.max_tokens = max_num_tokens;
+  z.row_pieces = hidden >> 4;
+  z.b_x = b_q;
+  if (launch_zero_pad(z, stream) != hipSuccess) return EP_ERR_LAUNCH;
+  ScalePadArgs zs{};
+  zs.tokens_per_expert = tokens_per_expert;
+  zs.E_local = num_local_experts;
+  zs.max_tokens = max_num_tokens;
+  zs.units = units;
+  zs.col_major = scale_col_major != 0;
+  zs.scale = static_cast<uint32_t*>(b_scale);
+  if (launch_scale_pad(zs, stream) != hipSuccess) return EP_ERR_LAUNCH;
+
+  RowArgs r{};
+  r.x = x;
+  r.T = num_tokens;
+  r.H = hidden;
+  r.token_row = token_row;
+  r.K = num_topk;
+  r.capacity = int64_t(num_local_experts) * max_num_tokens;
+  r.out = b_q;
+  r.out_scale = b_scale;
+  r.sparse = true;
+  r.scale_fmt = scale_fmt == EP_SCALE_UE8M0 ? kScaleUe8m0
+                : scale_fmt == EP_SCALE_POW2 ? kScalePow2 : kScaleF32;
+  r.scale_block_rows = scale_col_major ? max_num_tokens : 0;
+  return launch_status(launch_permute_fp8(r, stream));
 }
 
 int ep_combine(const void* y, int64_t num_rows, const int32_t* token_row,

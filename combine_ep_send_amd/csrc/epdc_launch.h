@@ -121,6 +121,10 @@ struct RegroupPadArgs {
 };
 hipError_t launch_regroup_pad(const RegroupPadArgs& a, hipStream_t s);
 
+// fp8 scale formats: fl32(amax/448); the smallest power of two at or above
+// it; that power as a UE8M0 byte, four packed per 32-bit word.
+enum : int { kScaleF32 = 0, kScalePow2 = 1, kScaleUe8m0 = 2 };
+
 struct RowArgs {
   const void* x;
   int64_t T;
@@ -129,8 +133,10 @@ struct RowArgs {
   int K;
   int64_t capacity;              // rows of the destination buffer
   void* out;
-  float* out_scale;              // fp8 scales or null
+  void* out_scale;               // fp8 scales (float or packed uint32) or null
   bool sparse;                   // many tokens have no destination: look up rows first
+  int scale_fmt;                 // kScale*
+  int64_t scale_block_rows;      // > 0: scales column-major per block of this many rows
 };
 hipError_t launch_permute_bf16(const RowArgs& a, hipStream_t s);
 hipError_t launch_permute_fp8(const RowArgs& a, hipStream_t s);
@@ -139,10 +145,23 @@ struct PadArgs {
   const int32_t* tokens_per_expert;  // [E_local] counts from the batched scan
   int E_local;
   int64_t max_tokens;
-  int H;
-  void* b_x;                         // [E_local, max_tokens, H] bf16
+  int64_t row_pieces;                // 16-byte pieces per row
+  void* b_x;                         // [E_local, max_tokens, row] rows
 };
 hipError_t launch_zero_pad(const PadArgs& a, hipStream_t s);
+
+// Zero scales of the padding slots of an expert-batched fp8 buffer: per
+// expert, max_tokens rows of `units` 32-bit scale words, row-major or
+// column-major ([units, max_tokens]).
+struct ScalePadArgs {
+  const int32_t* tokens_per_expert;
+  int E_local;
+  int64_t max_tokens;
+  int units;
+  bool col_major;
+  uint32_t* scale;
+};
+hipError_t launch_scale_pad(const ScalePadArgs& a, hipStream_t s);
 
 // Largest workgroup of the combine (one 16-byte piece per thread).
 constexpr int kMaxRowBlock = 1024;

@@ -106,26 +106,58 @@ __global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, 
 // of bf16 in, 16 bytes of e4m3 out); 8 lanes form one 128-channel group and
 // reduce its amax with three xor shuffles.  One wave per (token, chunk of
 // 64*IT 16-channel pieces); the chunk is quantized once and stored to every
-// send row of the token.
+// row of the token.
+//
+// Scales: fl32(amax/448) (SFMT kScaleF32); the smallest power of two at or
+// above it (kScalePow2); or that power's UE8M0 byte, exponent + 127 and at
+// least 0, i.e. 2^-127 (kScaleUe8m0), with the codes divided by the byte's
+// value.  UE8M0 bytes of groups 4j..4j+3 go into 32-bit word j, group 4j in
+// the low byte; a chunk starts on a multiple of 64 pieces, so the four
+// groups of a word always sit in lanes L, L+8, L+16, L+24 of one wave.  An
+// all-zero group has codes 0x00 and scale 0 (byte 0).
+//
+// Scale words of row r sit at r*units + u (row-major), or, with
+// scale_block_rows = M > 0, at (r/M)*M*units + u*M + r%M: each block of M
+// rows (an expert's slots) stores its scales column-major.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return a | (b << 8) | (c << 16) | (d << 24);
 }
 
-template <int KMAX, int IT>
+// Smallest power of two at or above s (s >= 0 and finite); 0 stays 0.  On
+// the bits: a normal value with a non-zero mantissa moves to the next
+// exponent; a subnormal mantissa m that is not a power of two becomes the
+// next power of two above m (2^23 being the smallest normal).
+__device__ __forceinline__ float pow2_ceil(float s) {
+  uint32_t u = __float_as_uint(s);
+  const uint32_t m = u & 0x7FFFFFu;
+  if (u >= 0x00800000u) {
+    if (m != 0u) u = (u & 0x7F800000u) + 0x00800000u;
+  } else if ((m & (m - 1u)) != 0u) {
+    u = 1u << (32 - __clz(m));
+  }
+  return __uint_as_float(u);
+}
+
+template <int KMAX, int IT, int SFMT, bool LOAD_FIRST>
 __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchunks,
                                                             int64_t item0) {
   const int lane = threadIdx.x;
   const int H8 = a.H >> 3;
   const int H16 = a.H >> 4;
-  const int G = a.H >> 7;
+  // scale words per row: one per group, or one per four groups (UE8M0)
+  const int units = SFMT == kScaleUe8m0 ? (a.H >> 9) : (a.H >> 7);
   u32x4* dq = static_cast<u32x4*>(a.out);
   const int64_t item = item0 + blockIdx.x;
   const int64_t t = udiv(item, nchunks);
   const int p0 = int(item - t * nchunks) * (kWave * IT);
-  // The row is loaded before its destinations are known (as in the bf16
-  // permute), so both round trips overlap.
+  // LOAD_FIRST: the row is loaded before its destinations are known (as in
+  // the bf16 permute), so both round trips overlap; the sparse
+  // expert-batched fill looks the rows up first and skips tokens with none.
   const u32x4* src = static_cast<const u32x4*>(a.x) + t * H8;
+  int32_t rows[KMAX];
+  bool use[KMAX];
+  if (!LOAD_FIRST && token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use) == 0) return;
   u32x4 in[IT][2];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -137,11 +169,9 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
       in[it][1] = ld_stream(src + 2 * p + 1);
     }
   }
-  int32_t rows[KMAX];
-  bool use[KMAX];
-  token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
+  if (LOAD_FIRST) token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
   u32x4 q[IT];
-  float sc[IT];
+  uint32_t sw[IT];   // this lane's scale word: float bits, or the packed bytes
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const uint32_t w[8] = {in[it][0].x, in[it][0].y, in[it][0].z, in[it][0].w,
@@ -158,25 +188,45 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     amax = fmaxf(amax, __shfl_xor(amax, 4));
-    const float scale = amax / 448.0f;
+    float scale = amax / 448.0f;
+    if (SFMT != kScaleF32) scale = pow2_ceil(scale);
+    float divisor = scale;
+    if (SFMT == kScaleUe8m0) {
+      const uint32_t byte = __float_as_uint(scale) >> 23;   // 0 below 2^-126
+      divisor = __uint_as_float(byte ? byte << 23 : 0x00400000u);
+      const uint32_t b1 = __shfl_down(byte, 8);
+      const uint32_t b2 = __shfl_down(byte, 16);
+      const uint32_t b3 = __shfl_down(byte, 24);
+      sw[it] = pack4(byte, b1, b2, b3);
+    } else {
+      sw[it] = __float_as_uint(scale);
+    }
     uint32_t c[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = scale > 0.0f ? e4m3_encode(f[i] / scale) : 0u;
+    for (int i = 0; i < 16; ++i) c[i] = amax > 0.0f ? e4m3_encode(f[i] / divisor) : 0u;
     q[it] = u32x4{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
                   pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15])};
-    sc[it] = scale;
   }
+  const int shift = SFMT == kScaleUe8m0 ? 5 : 3;      // pieces per scale word: 32 or 8
+  uint32_t* sbase = static_cast<uint32_t*>(a.out_scale);
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     if (!use[k]) continue;
-    u32x4* drow = dq + int64_t(rows[k]) * H16;
-    float* srow = a.out_scale + int64_t(rows[k]) * G;
+    const int64_t r = rows[k];
+    u32x4* drow = dq + r * H16;
+    int64_t s0 = r * units, ustride = 1;
+    if (a.scale_block_rows > 0) {
+      const int64_t M = a.scale_block_rows;
+      const int64_t blk = udiv(r, int(M));
+      s0 = blk * M * units + (r - blk * M);
+      ustride = M;
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int p = p0 + it * kWave + lane;
       if (p < H16) {
         st_stream(drow + p, q[it]);
-        if ((lane & 7) == 0) srow[p >> 3] = sc[it];
+        if ((p & ((1 << shift) - 1)) == 0) sbase[s0 + int64_t(p >> shift) * ustride] = sw[it];
       }
     }
   }
@@ -193,12 +243,32 @@ __global__ __launch_bounds__(kBlock) void zero_pad_kernel(PadArgs a) {
   const int e = blockIdx.y;
   int64_t cnt = a.tokens_per_expert[e];
   if (cnt > a.max_tokens) cnt = a.max_tokens;
-  const int64_t H8 = a.H >> 3;
-  const int64_t region = a.max_tokens * H8;
+  const int64_t per_row = a.row_pieces;
+  const int64_t region = a.max_tokens * per_row;
   u32x4* base = static_cast<u32x4*>(a.b_x) + int64_t(e) * region;
   for (int64_t v = int64_t(blockIdx.x) * kBlock + threadIdx.x; v < region;
        v += int64_t(gridDim.x) * kBlock) {
-    if (v >= cnt * H8) base[v] = u32x4{0u, 0u, 0u, 0u};
+    if (v >= cnt * per_row) base[v] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Zero scale words of the padding slots.  Row-major, expert e's padding is
+// one run [cnt*units, max*units); column-major it is one run [u*max + cnt,
+// (u+1)*max) per scale word u.  Grid (chunks of the longest run, E_local);
+// each workgroup stores its chunk of every run of its expert.
+__global__ __launch_bounds__(kBlock) void scale_pad_kernel(ScalePadArgs a) {
+  const int e = blockIdx.y;
+  int64_t cnt = a.tokens_per_expert[e];
+  if (cnt > a.max_tokens) cnt = a.max_tokens;
+  const int64_t M = a.max_tokens;
+  uint32_t* base = a.scale + int64_t(e) * M * a.units;
+  const int runs = a.col_major ? a.units : 1;
+  const int64_t len = a.col_major ? M - cnt : (M - cnt) * a.units;
+  const int64_t v = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  if (v >= len) return;
+  for (int u = 0; u < runs; ++u) {
+    const int64_t start = a.col_major ? int64_t(u) * M + cnt : cnt * a.units;
+    base[start + v] = 0u;
   }
 }
 
@@ -435,10 +505,13 @@ void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
   });
 }
 
-template <int KMAX, int IT>
+template <int KMAX, int IT, int SFMT>
 void launch_permute_fp8_p(const RowArgs& a, Split sp, hipStream_t s) {
   for_each_launch(a.T * sp.nchunks, [&](int64_t i0, unsigned g) {
-    permute_fp8_kernel<KMAX, IT><<<g, kWave, 0, s>>>(a, sp.nchunks, i0);
+    if (a.sparse)
+      permute_fp8_kernel<KMAX, IT, SFMT, false><<<g, kWave, 0, s>>>(a, sp.nchunks, i0);
+    else
+      permute_fp8_kernel<KMAX, IT, SFMT, true><<<g, kWave, 0, s>>>(a, sp.nchunks, i0);
   });
 }
 
@@ -447,7 +520,13 @@ void launch_permute_fp8_k(const RowArgs& a, hipStream_t s) {
   // One 16-channel piece per lane, one wave per 1024 channels (7 per 7168-
   // channel row): the fastest of the shapes measured (1-7 pieces per lane,
   // 1-7 waves per workgroup) on the cache-cleared 8k-token chunk.
-  launch_permute_fp8_p<KMAX, 1>(a, split_row(a.H >> 4, 1), s);
+  const Split sp = split_row(a.H >> 4, 1);
+  if (a.scale_fmt == kScaleUe8m0)
+    launch_permute_fp8_p<KMAX, 1, kScaleUe8m0>(a, sp, s);
+  else if (a.scale_fmt == kScalePow2)
+    launch_permute_fp8_p<KMAX, 1, kScalePow2>(a, sp, s);
+  else
+    launch_permute_fp8_p<KMAX, 1, kScaleF32>(a, sp, s);
 }
 
 template <int KMAX>
@@ -524,11 +603,21 @@ hipError_t launch_permute_fp8(const RowArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_zero_pad(const PadArgs& a, hipStream_t s) {
-  const int64_t region = a.max_tokens * (a.H >> 3);
+  const int64_t region = a.max_tokens * a.row_pieces;
   if (region == 0 || a.E_local == 0) return hipSuccess;
   const int64_t gx = (region + kBlock - 1) / kBlock;
   const dim3 grid{unsigned(gx < kMaxGrid ? gx : kMaxGrid), unsigned(a.E_local), 1u};
   zero_pad_kernel<<<grid, kBlock, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_pad(const ScalePadArgs& a, hipStream_t s) {
+  const int64_t longest = a.col_major ? a.max_tokens : a.max_tokens * a.units;
+  if (longest == 0 || a.E_local == 0) return hipSuccess;
+  const int64_t gx = (longest + kBlock - 1) / kBlock;
+  if (gx > kMaxGrid) return hipErrorInvalidValue;
+  const dim3 grid{unsigned(gx), unsigned(a.E_local), 1u};
+  scale_pad_kernel<<<grid, kBlock, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ from typing import Callable, List, NamedTuple, Optional, Tuple
 
 import torch
 
-from .ops import (Regrouped, ep_batched_prepare, ep_build_send_layout, ep_combine,
+from .ops import (Regrouped, ep_batched_prepare, ep_batched_prepare_fp8, ep_build_send_layout,
+                  ep_combine,
                   ep_compute_send_counts, ep_dispatch_layout, ep_dispatch_permute,
                   ep_regroup_by_expert)
 
@@ -198,11 +199,19 @@ def dispatch_chunked_forward(x: torch.Tensor, topk_idx: torch.Tensor, topk_weigh
 
 
 def batched_prepare(a1: torch.Tensor, topk_ids: torch.Tensor, *, num_local_experts: int,
-                    rank: int, max_num_tokens: int):
-    """vLLM BatchedPrepareAndFinalize.prepare (unquantized): returns
-    (b_a1 [E_local, max, H], tokens_per_expert [E_local], token_row [T,K])."""
+                    rank: int, max_num_tokens: int, quant: Optional[str] = None,
+                    scale_col_major: bool = False):
+    """vLLM BatchedPrepareAndFinalize.prepare.  Unquantized: returns (b_a1
+    [E_local, max, H] bf16, tokens_per_expert [E_local], token_row [T,K]).
+    With ``quant`` = "f32", "pow2" or "ue8m0" the rows are fp8 e4m3 with one
+    scale per token per 128 channels (NeMo uccl_ep Buffer.low_latency_dispatch
+    use_fp8 / round_scale / use_ue8m0), and the return value is (b_q,
+    b_scale, tokens_per_expert, token_row)."""
     first = int(rank) * int(num_local_experts)
-    return ep_batched_prepare(a1, topk_ids, first, num_local_experts, max_num_tokens)
+    if quant is None:
+        return ep_batched_prepare(a1, topk_ids, first, num_local_experts, max_num_tokens)
+    return ep_batched_prepare_fp8(a1, topk_ids, first, num_local_experts, max_num_tokens,
+                                  scale_fmt=quant, scale_col_major=scale_col_major)
 
 
 def batched_finalize(fused_expert_output: torch.Tensor, topk_weights: torch.Tensor,

@@ -13,7 +13,8 @@ from typing import NamedTuple, Optional
 
 import torch
 
-from ._lib import EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3, check, lib
+from ._lib import (EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3, EP_SCALE_F32, EP_SCALE_POW2, EP_SCALE_UE8M0,
+                   check, lib)
 
 __all__ = [
     "Counts",
@@ -27,6 +28,9 @@ __all__ = [
     "ep_regroup_workspace_bytes",
     "Regrouped",
     "ep_batched_prepare",
+    "ep_batched_prepare_fp8",
+    "batched_scale_like",
+    "SCALE_FORMATS",
     "ep_combine",
     "ep_counts_workspace_bytes",
     "ep_layout_workspace_bytes",
@@ -414,6 +418,76 @@ def ep_batched_prepare(x: torch.Tensor, topk_idx: torch.Tensor, first_expert: in
         _stream(stream))
     check(st, "ep_batched_prepare")
     return out, tokens_per_expert, token_row
+
+
+SCALE_FORMATS = {"f32": EP_SCALE_F32, "pow2": EP_SCALE_POW2, "ue8m0": EP_SCALE_UE8M0}
+
+
+def batched_scale_like(num_local_experts: int, max_num_tokens: int, hidden: int,
+                       scale_fmt: str = "f32", col_major: bool = False,
+                       device=None) -> torch.Tensor:
+    """An empty scale tensor for ep_batched_prepare_fp8: [E_local, max, H/128]
+    float32, or [E_local, max, H/512] int32 for ``ue8m0``; with ``col_major``
+    the last two dimensions are stored column-major (a transposed view of
+    [E_local, units, max])."""
+    units = hidden // (512 if scale_fmt == "ue8m0" else 128)
+    dt = torch.int32 if scale_fmt == "ue8m0" else torch.float32
+    El, M = int(num_local_experts), int(max_num_tokens)
+    if col_major:
+        return torch.empty((El, units, M), dtype=dt, device=device).transpose(1, 2)
+    return torch.empty((El, M, units), dtype=dt, device=device)
+
+
+def ep_batched_prepare_fp8(x: torch.Tensor, topk_idx: torch.Tensor, first_expert: int,
+                           num_local_experts: int, max_num_tokens: int, *,
+                           scale_fmt: str = "f32", scale_col_major: bool = False,
+                           out: Optional[torch.Tensor] = None,
+                           out_scale: Optional[torch.Tensor] = None,
+                           tokens_per_expert: Optional[torch.Tensor] = None,
+                           token_row: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """The expert-batched layout with fp8 rows.  Returns (b_q [E_local, max, H]
+    float8_e4m3fn, b_scale (see batched_scale_like), tokens_per_expert
+    [E_local] int32, token_row [T, K] int32).  ``scale_fmt`` is "f32",
+    "pow2" (power-of-two scales) or "ue8m0" (packed UE8M0 bytes)."""
+    if scale_fmt not in SCALE_FORMATS:
+        raise ValueError(f"scale_fmt must be one of {sorted(SCALE_FORMATS)}")
+    _gpu(x, "x", torch.bfloat16, 2)
+    _gpu(topk_idx, "topk_idx", torch.int64, 2)
+    T, H = x.shape
+    if topk_idx.shape[0] != T:
+        raise ValueError("topk_idx must be [T, K]")
+    K = topk_idx.shape[1]
+    El, M = int(num_local_experts), int(max_num_tokens)
+    dev = x.device
+    if out is None:
+        out = torch.empty((El, M, H), dtype=torch.float8_e4m3fn, device=dev)
+    if out_scale is None:
+        out_scale = batched_scale_like(El, M, H, scale_fmt, scale_col_major, dev)
+    if tokens_per_expert is None:
+        tokens_per_expert = torch.empty(El, dtype=torch.int32, device=dev)
+    if token_row is None:
+        token_row = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _shape(_gpu(out, "b_q", torch.float8_e4m3fn), "b_q", (El, M, H))
+    like = batched_scale_like(El, M, H, scale_fmt, scale_col_major, "meta")
+    if out_scale.device != dev or out_scale.dtype != like.dtype or \
+            tuple(out_scale.shape) != tuple(like.shape) or \
+            (out_scale.numel() and out_scale.stride() != like.stride()):
+        raise ValueError(f"b_scale must be {like.dtype} {tuple(like.shape)} with strides "
+                         f"{like.stride()} on {dev}")
+    _shape(_gpu(tokens_per_expert, "tokens_per_expert", torch.int32), "tokens_per_expert", (El,))
+    _shape(_gpu(token_row, "token_row", torch.int32), "token_row", (T, K))
+    nbytes = ep_batched_workspace_bytes(T, El, M)
+    if workspace is None:
+        workspace = workspace_for(nbytes, dev, stream)
+    _gpu(workspace, "workspace", torch.uint8)
+    st = lib().ep_batched_prepare_fp8(
+        _vp(x), _vp(topk_idx), T, K, H, int(first_expert), El, M, SCALE_FORMATS[scale_fmt],
+        1 if scale_col_major else 0, _vp(out), out_scale.data_ptr() if out_scale.numel() else None,
+        _vp(tokens_per_expert), _vp(token_row), _vp(workspace), workspace.numel(),
+        _stream(stream))
+    check(st, "ep_batched_prepare_fp8")
+    return out, out_scale, tokens_per_expert, token_row
 
 
 def ep_combine(y: torch.Tensor, token_row: torch.Tensor,

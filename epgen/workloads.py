@@ -52,6 +52,8 @@ class WorkloadSpec:
     first_expert: int = 0       # batched layout: first local expert
     max_num_tokens: int = 0     # batched layout: rows per local expert
     fp8: bool = False           # quantise rows to e4m3 on dispatch
+    scale_fmt: str = "f32"      # fp8 scales: "f32", "pow2" or "ue8m0"
+    scale_col_major: bool = False  # batched fp8: scales column-major per expert
     align: int = 1              # expert-major layout: rows per expert padded to a multiple
     chunks: int = 1             # contiguous token chunks
     streams: int = 1            # HIP streams the chunks alternate over
@@ -72,6 +74,10 @@ CONFIGS = {
     "batched_t8192": WorkloadSpec(
         "batched_t8192", T=8192, H=7168, E=256, K=8, P=8, layout="batched",
         first_expert=0, max_num_tokens=8192),
+    "batched_fp8_t8192": WorkloadSpec(
+        "batched_fp8_t8192", T=8192, H=7168, E=256, K=8, P=8, layout="batched",
+        first_expert=0, max_num_tokens=8192, fp8=True, scale_fmt="ue8m0",
+        scale_col_major=True),
     "skewed_t16384": WorkloadSpec(
         "skewed_t16384", T=16384, H=7168, E=256, K=8, P=32, routing="zipf",
         zipf_s=1.2, unrouted_frac=0.05),

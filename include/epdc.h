@@ -15,7 +15,8 @@
  *    combine, chunk_bounds, dispatch_chunked_forward, to_host.
  *  - NeMo AutoModel API docs, "nemo_automodel.components.moe.uccl_ep.buffer":
  *    Buffer.get_dispatch_layout, Buffer.dispatch, Buffer.combine,
- *    Buffer.low_latency_dispatch (fp8 rows + float scales per 128 channels).
+ *    Buffer.low_latency_dispatch (fp8 rows + scales per 128 channels: float,
+ *    power-of-two, or packed UE8M0).
  *  - vLLM API docs, "vllm.model_executor.layers.fused_moe.prepare_finalize":
  *    BatchedPrepareAndFinalize.prepare / finalize.
  *  - NeMo AutoModel API docs,
@@ -72,7 +73,13 @@ typedef enum {
     EP_DTYPE_FP8_E4M3 = 1      /* OCP e4m3 (float8_e4m3fn) + fp32 scales */
 } ep_dtype_t;
 
-#define EPDC_ABI_VERSION 2
+typedef enum {
+    EP_SCALE_F32 = 0,          /* fp32 scale = amax / 448 */
+    EP_SCALE_POW2 = 1,         /* fp32 scale, rounded up to a power of two */
+    EP_SCALE_UE8M0 = 2         /* that power as a UE8M0 byte, 4 per int32 */
+} ep_scale_fmt_t;
+
+#define EPDC_ABI_VERSION 3
 #define EPDC_MAX_TOPK 16
 #define EPDC_MAX_BINS 1024
 #define EPDC_FP8_GROUP 128
@@ -335,6 +342,55 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx,
                        int32_t* tokens_per_expert, int32_t* token_row,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/*
+ * Expert-batched layout with fp8 rows: [E_local, max_num_tokens, H] e4m3
+ * codes plus one scale per 128 channels.
+ * NeMo "uccl_ep.buffer": Buffer.low_latency_dispatch with use_fp8 (rows
+ * [E_local, max, H] float8_e4m3fn; scales [E_local, max, H/128] float, or
+ * with use_ue8m0 packed [E_local, max, H/512] int; round_scale makes the
+ * scales powers of two; the last two dimensions of the scales may be stored
+ * column-major); vLLM "fused_moe.prepare_finalize":
+ * BatchedPrepareAndFinalize.prepare, quantized branch (zeroed buffers, the
+ * rows of each expert quantized per token with groups of 128 channels).
+ *
+ * The slots, counts and token_row are those of ep_batched_prepare; slot s of
+ * expert e holds the quantized row of its token.  Per row and group g of 128
+ * channels: amax = max |x|, s = fp32(amax / 448), and
+ *   EP_SCALE_F32    scale = s, stored as fp32 [E_local, max, H/128];
+ *   EP_SCALE_POW2   scale = the smallest power of two >= s, stored as fp32;
+ *   EP_SCALE_UE8M0  the same power 2^e stored as the byte max(e + 127, 0)
+ *                   (so scales below 2^-127 become 2^-127), four bytes per
+ *                   int32 (groups 4j..4j+3 of word j, 4j in the low byte):
+ *                   [E_local, max, H/512] int32; H must be a multiple of 512.
+ * code = e4m3(fp32(x / scale)) with scale the stored value (2^(byte-127) for
+ * UE8M0), rounded to nearest, ties to even, saturating at +-448, sign kept;
+ * amax == 0 gives codes 0x00 and scale 0 (byte 0).  Inputs must be finite.
+ * Every padding slot (past an expert's count) gets zero codes and zero
+ * scale words, each byte written once.
+ *
+ *   x                  [T,H] bf16 in
+ *   topk_idx           [T,K] int64 in
+ *   first_expert       global id of local expert 0
+ *   scale_fmt          EP_SCALE_F32, EP_SCALE_POW2 or EP_SCALE_UE8M0
+ *   scale_col_major    0: b_scale row-major [E_local, max, units];
+ *                      1: each expert's block stored as [units, max], i.e.
+ *                      word u of slot s of expert e at (e*units + u)*max + s
+ *                      (units = H/128, or H/512 for UE8M0)
+ *   b_q                [E_local, max_num_tokens, H] uint8 out (16-byte aligned)
+ *   b_scale            the scale words described above, out
+ *   tokens_per_expert  [E_local] int32 out  true counts (may exceed max)
+ *   token_row          [T,K] int32 out  e*max_num_tokens + slot, or -1
+ *   workspace          ep_batched_workspace_bytes(T, E_local, max) bytes
+ */
+int ep_batched_prepare_fp8(const void* x, const int64_t* topk_idx,
+                           int64_t num_tokens, int num_topk, int hidden,
+                           int first_expert, int num_local_experts,
+                           int64_t max_num_tokens, int scale_fmt,
+                           int scale_col_major, void* b_q, void* b_scale,
+                           int32_t* tokens_per_expert, int32_t* token_row,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * Combine back onto the source tokens, weighted or as per-destination

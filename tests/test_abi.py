@@ -18,7 +18,7 @@ EXPECTED = {
     "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
     "ep_dispatch_layout_workspace_bytes", "ep_dispatch_layout",
     "ep_regroup_workspace_bytes", "ep_regroup_by_expert",
-    "ep_dispatch_permute", "ep_batched_prepare", "ep_combine",
+    "ep_dispatch_permute", "ep_batched_prepare", "ep_batched_prepare_fp8", "ep_combine",
 }
 
 
@@ -37,9 +37,9 @@ def test_library_exports_every_header_function():
 
 
 def test_version_and_status_strings():
-    # version 2: ep_combine takes optional weights and biases
+    # version 3: ep_batched_prepare_fp8 and the scale formats
     L = _lib.lib()
-    assert L.ep_abi_version() == 2
+    assert L.ep_abi_version() == 3
     assert L.ep_status_string(0) == b"ok"
     for s in (-1, -2, -3, -4):
         assert L.ep_status_string(s) not in (b"ok", b"unknown status")
@@ -185,3 +185,23 @@ def test_batched_rejects_bad_arguments():
     assert call(El=2000) == _lib.EP_ERR_UNSUPPORTED
     assert call(M=1 << 30) == _lib.EP_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.EP_ERR_WORKSPACE
+
+
+def test_batched_fp8_rejects_bad_arguments():
+    L = _lib.lib()
+    f = L.ep_batched_prepare_fp8
+
+    def call(H=512, fmt=0, col=0, first=0, El=4, M=8, q=A16, sc=A16, ws=A16, ws_bytes=1 << 20):
+        return f(A16, A16, 16, 2, H, first, El, M, fmt, col, q, sc, A16, A16, ws, ws_bytes, None)
+    assert call(H=64) == _lib.EP_ERR_INVALID_ARG                  # H % 128
+    assert call(H=640, fmt=2) == _lib.EP_ERR_INVALID_ARG          # UE8M0: H % 512
+    assert call(fmt=3) == _lib.EP_ERR_INVALID_ARG
+    assert call(col=2) == _lib.EP_ERR_INVALID_ARG
+    assert call(first=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(El=2000) == _lib.EP_ERR_UNSUPPORTED
+    assert call(M=1 << 30) == _lib.EP_ERR_UNSUPPORTED
+    assert call(q=A8) == _lib.EP_ERR_INVALID_ARG
+    assert call(sc=None) == _lib.EP_ERR_INVALID_ARG
+    assert call(sc=ODD) == _lib.EP_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.EP_ERR_WORKSPACE
+    assert call(ws_bytes=16) == _lib.EP_ERR_WORKSPACE
