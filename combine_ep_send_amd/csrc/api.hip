@@ -36,6 +36,18 @@ int check_hidden(int H, bool fp8) {
   return EP_OK;
 }
 
+// Control header, published rows, per-group prefixes and bin totals of the
+// fused launch, laid out as ep_*_workspace_bytes sizes them.
+void set_fused_workspace(FusedArgs& a, void* ws, int64_t tiles, int64_t bins, int64_t row_words,
+                         int64_t groups) {
+  const int64_t gcap = tiles < kMaxFusedGroups ? tiles : kMaxFusedGroups;
+  a.ctrl = static_cast<uint32_t*>(ws);
+  a.rows = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kWsHeaderBytes);
+  a.pref = a.rows + gcap * row_words;
+  a.tots = a.pref + gcap * bins;
+  a.two_pass = fused_two_pass(groups, bins);
+}
+
 int64_t fused_tiles(int64_t T) {
   const int64_t t = (T + 255) / 256;   // tiles of 256 tokens
   return t > 0 ? t : 1;
@@ -171,10 +183,8 @@ int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights, con
 size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
                                           int num_local_experts) {
   if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1) return 0;
-  const int64_t groups = fused_tiles(num_tokens) < kMaxFusedGroups ? fused_tiles(num_tokens)
-                                                                    : kMaxFusedGroups;
   const int64_t nh = int64_t(num_ranks) + int64_t(num_ranks) * num_local_experts + 1;
-  return kWsHeaderBytes + size_t(groups) * size_t(nh) * 4u;
+  return fused_ws_bytes(fused_tiles(num_tokens), num_ranks, nh);
 }
 
 int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64_t num_tokens,
@@ -236,8 +246,7 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
   a.token_row = token_row;
   a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
   a.vec_in = (num_topk % 4) == 0 && aligned(topk_idx, 16) && aligned(topk_weights, 16);
-  a.ctrl = static_cast<uint32_t*>(workspace);
-  a.rows = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
+  set_fused_workspace(a, workspace, tiles, num_ranks, int64_t(num_ranks) + E + 1, groups);
   a.tiles = tiles;
   a.tiles_per_group = int(per);
   return launch_status(launch_dispatch_layout(a, unsigned(groups), stream));
@@ -245,9 +254,7 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
 
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins) {
   if (num_rows < 0 || num_bins < 1) return 0;
-  const int64_t groups = fused_tiles(num_rows) < kMaxFusedGroups ? fused_tiles(num_rows)
-                                                                  : kMaxFusedGroups;
-  return kWsHeaderBytes + size_t(groups) * size_t(num_bins + 1) * 4u;
+  return fused_ws_bytes(fused_tiles(num_rows), num_bins, int64_t(num_bins) + 1);
 }
 
 int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const float* recv_w,
@@ -302,8 +309,7 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   a.send_counts = tokens_per_expert;
   a.send_token_idx = perm_src;
   a.token_row = row_map;
-  a.ctrl = static_cast<uint32_t*>(workspace);
-  a.rows = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kWsHeaderBytes);
+  set_fused_workspace(a, workspace, tiles, bins, int64_t(bins) + 1, groups);
   a.tiles = tiles;
   a.tiles_per_group = int(per);
   a.ids32 = recv_idx;

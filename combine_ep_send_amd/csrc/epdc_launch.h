@@ -92,6 +92,9 @@ struct FusedArgs {
   bool vec_in;                   // K % 4 == 0 and topk_idx/topk_weights 16-byte aligned
   uint32_t* ctrl;                // workspace header: [0] arrivals, [2] barrier generation
   uint32_t* rows;                // [groups, P + E + 1] published totals
+  uint32_t* pref;                // [groups, P] per-group exclusive prefixes (two-pass scan)
+  uint32_t* tots;                // [P] bin totals (two-pass scan)
+  bool two_pass;                 // scan the rows bin by bin, with a second barrier
   int64_t tiles;                 // tiles of 256 tokens (>= 1)
   int tiles_per_group;
   // regroup by local expert (P = E_local bins, E = 0)
@@ -104,6 +107,18 @@ struct FusedArgs {
 // Workgroups of the fused counts + layout launch: at most one per compute
 // unit and at most kMaxFusedGroups, so that all of them are resident at once.
 constexpr int kMaxFusedGroups = 256;
+// Bins one workgroup scans in the two-pass form (at most).
+constexpr int kMaxTwoPassBins = 8;
+// Workspace of the fused launch: header, rows, prefixes, totals.
+inline size_t fused_ws_bytes(int64_t tiles, int64_t bins, int64_t row_words) {
+  const int64_t g = tiles < kMaxFusedGroups ? tiles : kMaxFusedGroups;
+  return kWsHeaderBytes + size_t(g) * size_t(row_words) * 4u + size_t(g) * size_t(bins) * 4u +
+         size_t(bins) * 4u;
+}
+// Whether a launch of `groups` workgroups over `bins` bins takes the two-pass scan.
+inline bool fused_two_pass(int64_t groups, int64_t bins) {
+  return groups * bins > 8 * 256 && (bins + groups - 1) / groups <= kMaxTwoPassBins;
+}
 size_t fused_smem_bytes(int P, int E, int tiles_per_group);
 hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
 hipError_t launch_regroup_layout(const FusedArgs& a, unsigned groups, hipStream_t s);

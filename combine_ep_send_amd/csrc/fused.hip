@@ -12,7 +12,9 @@
 //     workgroup per compute unit, so all of them are resident together.
 //  3. Each workgroup reads the rows: the destination totals give the segment
 //     starts, the rows of lower workgroups its base inside each segment.  A
-//     slice of the experts is summed by every workgroup.
+//     slice of the experts is summed by every workgroup.  With many groups
+//     and bins the rows are instead scanned bin by bin, one slice of bins
+//     per workgroup, and read back after a second barrier.
 //  4. It ranks its tokens again and writes token_row and the send rows
 //     token-major.
 //
@@ -33,6 +35,59 @@ namespace epdc {
 namespace {
 
 constexpr uint32_t kBarrierSpinLimit = 1u << 22;   // sleeps (~0.1 s), then give up
+
+// Grid-wide barrier number k (1, 2, ...) of this launch.  Thread 0 of every
+// workgroup adds one arrival; the arrival that completes barrier k (the
+// (k*G)-th of the launch) publishes generation gen + k, the others wait for
+// it.  The launch's last barrier also clears the arrivals for the next call.
+// A wait that outlasts the spin limit sets an error bit instead of hanging.
+__device__ __forceinline__ void grid_sync(uint32_t* ctrl, int G, uint32_t gen, uint32_t k,
+                                          bool last) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are performed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (fetch_add_relaxed(&ctrl[kCtrlTicket], 1u) == k * uint32_t(G) - 1u) {
+      if (last) st_relaxed(&ctrl[kCtrlTicket], 0u);
+      st_relaxed(&ctrl[kCtrlEpoch], gen + k);
+    } else {
+      uint32_t spins = 0;
+      while (ld_relaxed(&ctrl[kCtrlEpoch]) == gen + k - 1u) {
+        if (++spins > kBarrierSpinLimit) {
+          fetch_or(&ctrl[kCtrlError], kErrLookbackGaveUp);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix sum over the workgroup's threads (thread order); `total`
+// receives the sum of all.  s_scan holds one word per wave.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_scan,
+                                                         uint32_t& total) {
+  const int lane = lane_id();
+  const int wave = wave_id();
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == kWave - 1) s_scan[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const uint32_t t = s_scan[w];
+    if (w < wave) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
 
 // One tile's slots: owning destination (bin), global id and weight.
 template <int KMAX>
@@ -143,6 +198,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   int32_t* s_tot = s_hist + nh;                                              // [P]
   int32_t* s_base = s_tot + P;                                               // [P]
   __shared__ int32_t s_bad;
+  __shared__ uint32_t s_scan[kWavesPerBlock];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -209,24 +265,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   for (int i = tid; i < nh; i += kBlock) st_relaxed(row_out + i, uint32_t(s_hist[i]));
 
   // ---- 2. grid barrier --------------------------------------------------------
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's row stores are performed
-  __syncthreads();
-  if (tid == 0) {
-    if (fetch_add_relaxed(&a.ctrl[kCtrlTicket], 1u) == uint32_t(G - 1)) {
-      st_relaxed(&a.ctrl[kCtrlTicket], 0u);
-      st_relaxed(&a.ctrl[kCtrlEpoch], gen + 1u);
-    } else {
-      uint32_t spins = 0;
-      while (ld_relaxed(&a.ctrl[kCtrlEpoch]) == gen) {
-        if (++spins > kBarrierSpinLimit) {
-          fetch_or(&a.ctrl[kCtrlError], kErrLookbackGaveUp);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-  }
-  __syncthreads();
+  grid_sync(a.ctrl, G, gen, 1, !a.two_pass);
 
   // ---- 3. totals, bases, expert slice -----------------------------------------
   // experts [e0, e1) are this workgroup's slice of the expert totals
@@ -241,7 +280,54 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   }
   for (int i = tid; i < ne; i += kBlock) s_etot[i] = 0;
   __syncthreads();
-  {
+  if (a.two_pass) {
+    // Many groups and bins: every workgroup reading all lower rows would
+    // take G*P loads each.  Instead workgroup g scans a slice of the bins
+    // over the groups (thread i holds group i's count; one load each), and
+    // publishes each group's exclusive prefix and the bin's total; after a
+    // second barrier every workgroup reads its own prefixes and the totals
+    // (P loads each).
+    const int per_b = (P + G - 1) / G;
+    const int b0 = g * per_b;
+    uint32_t v[kMaxTwoPassBins];
+#pragma unroll
+    for (int u = 0; u < kMaxTwoPassBins; ++u) {
+      const int b = b0 + u;
+      v[u] = (u < per_b && b < P && tid < G) ? ld_relaxed(a.rows + int64_t(tid) * nh + b) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxTwoPassBins; ++u) {
+      const int b = b0 + u;
+      if (u >= per_b || b >= P) break;             // uniform across the workgroup
+      uint32_t total = 0;
+      const uint32_t ex = block_exclusive_scan(v[u], s_scan, total);
+      if (tid < G) st_relaxed(a.pref + int64_t(tid) * P + b, ex);
+      if (tid == 0) st_relaxed(a.tots + b, total);
+    }
+    // the expert slice, as in the single pass
+    for (int i0 = tid; i0 < G * ne; i0 += kBlock * 8) {
+      uint32_t vx[8];
+      int ex[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kBlock;
+        vx[u] = 0u;
+        ex[u] = 0;
+        if (i < G * ne) {
+          ex[u] = i % ne;
+          vx[u] = ld_relaxed(a.rows + int64_t(i / ne) * nh + P + e0 + ex[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (vx[u]) atomicAdd(&s_etot[ex[u]], int(vx[u]));
+    }
+    grid_sync(a.ctrl, G, gen, 2, true);
+    for (int b = tid; b < P; b += kBlock) {
+      s_base[b] = int(ld_relaxed(a.pref + int64_t(g) * P + b));
+      s_tot[b] = int(ld_relaxed(a.tots + b));
+    }
+  } else {
     // (group, destination) and (group, expert of the slice) pairs, all loads
     // of a batch in flight together; groups start at different rows so the
     // same words are not all requested at once.

@@ -106,9 +106,11 @@ def test_layout_rejects_bad_workspace_and_capacity():
 def test_fused_layout_workspace_and_arguments():
     L = _lib.lib()
     # one row of P + E + 1 words per workgroup, min(tiles of 256, 256) rows
-    assert L.ep_dispatch_layout_workspace_bytes(16384, 32, 8) == 256 + 64 * (32 + 256 + 1) * 4
-    assert L.ep_dispatch_layout_workspace_bytes(0, 2, 4) == 256 + 1 * (2 + 8 + 1) * 4
-    assert L.ep_dispatch_layout_workspace_bytes(1 << 20, 8, 8) == 256 + 256 * (8 + 64 + 1) * 4
+    assert L.ep_dispatch_layout_workspace_bytes(16384, 32, 8) == \
+        256 + 64 * (32 + 256 + 1) * 4 + 64 * 32 * 4 + 32 * 4
+    assert L.ep_dispatch_layout_workspace_bytes(0, 2, 4) == 256 + 1 * (2 + 8 + 1) * 4 + 2 * 4 + 2 * 4
+    assert L.ep_dispatch_layout_workspace_bytes(1 << 20, 8, 8) == \
+        256 + 256 * (8 + 64 + 1) * 4 + 256 * 8 * 4 + 8 * 4
     assert L.ep_dispatch_layout_workspace_bytes(-1, 2, 4) == 0
     f = L.ep_dispatch_layout
 
@@ -132,8 +134,8 @@ def test_fused_layout_workspace_and_arguments():
 
 def test_regroup_workspace_and_arguments():
     L = _lib.lib()
-    assert L.ep_regroup_workspace_bytes(1000, 8) == 256 + 4 * (8 + 1) * 4
-    assert L.ep_regroup_workspace_bytes(0, 8) == 256 + 1 * 9 * 4
+    assert L.ep_regroup_workspace_bytes(1000, 8) == 256 + 4 * (8 + 1) * 4 + 4 * 8 * 4 + 8 * 4
+    assert L.ep_regroup_workspace_bytes(0, 8) == 256 + 1 * 9 * 4 + 8 * 4 + 8 * 4
     assert L.ep_regroup_workspace_bytes(10, 0) == 0
     f = L.ep_regroup_by_expert
 

@@ -84,6 +84,9 @@ def check_fused(idx, w, P, El, cap=None, workspace=None):
     (700, 30, 5, 6, "uniform", 0.0),          # P not a multiple of 4
     (1, 8, 2, 2, "uniform", 0.0),             # a single token
     (76800, 16, 2, 4, "uniform", 0.0),        # 300 tiles: two tiles per workgroup
+    (20000, 256, 8, 64, "zipf", 0.05),        # 79 groups x 64 bins: the two-pass scan
+    (8192, 256, 8, 256, "uniform", 0.0),      # 32 groups x 256 bins: 8 bins per group
+    (3000, 1024, 4, 512, "uniform", 0.0),     # 12 groups x 512 bins: single pass, many loads
 ])
 def test_fused_layout_matches_oracle(T, E, K, P, routing, unrouted):
     print(f"case: T={T} E={E} K={K} P={P} {routing}", flush=True)
@@ -149,8 +152,19 @@ def test_fused_bad_ids_and_empty():
     assert c["diag"][0] == 0
 
 
+def _barriers(T, P):
+    """Grid barriers one fused call takes: two when its groups x bins table
+    is scanned bin by bin (more than 2048 entries, at most 8 bins per group)."""
+    tiles = max(1, -(-T // 256))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per = -(-tiles // min(cus, 256))
+    groups = -(-tiles // per)
+    return 2 if groups * P > 2048 and -(-P // groups) <= 8 else 1
+
+
 def test_fused_workspace_reused_across_calls_and_sizes():
-    sizes = [(5000, 64), (37, 8), (70000, 4), (1, 2), (2999, 64), (256, 32)]
+    sizes = [(5000, 64), (37, 8), (20000, 64), (70000, 4), (1, 2), (2999, 64), (256, 32),
+             (20000, 128)]
     nbytes = max(ep.ep_dispatch_layout_workspace_bytes(T, P, 2) for T, P in sizes)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     for i, (T, P) in enumerate(sizes):
@@ -158,4 +172,6 @@ def test_fused_workspace_reused_across_calls_and_sizes():
         check_fused(idx, w, P, 2, workspace=ws)
     hdr = ws[:16].view(torch.int32).cpu().numpy()
     assert hdr[0] == 0 and hdr[3] == 0        # arrivals rearmed, no barrier time-out
-    assert hdr[2] == len(sizes)               # one barrier generation per call
+    want = sum(_barriers(T, P) for T, P in sizes)
+    assert want > len(sizes)                  # some calls took the two-pass scan
+    assert hdr[2] == want                     # one generation per barrier
