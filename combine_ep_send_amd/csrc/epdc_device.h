@@ -26,6 +26,30 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Per-bin ballots of a wave, all 64 at once: lane i holds a mask m whose bit
+// j says "lane i belongs to bin j"; lane j receives the ballot of bin j (bit
+// i set when lane i's mask has bit j).  That is the transpose of a 64x64
+// bit matrix, done in six exchange steps: at step s the lanes i and i^s swap
+// the s-by-s blocks that lie off the diagonal.  It replaces 64 ballots.
+__device__ __forceinline__ uint64_t wave_bin_ballots(uint64_t m) {
+  const int lane = int(threadIdx.x) & (kWave - 1);
+  constexpr uint64_t kBlockMask[6] = {0x00000000FFFFFFFFull, 0x0000FFFF0000FFFFull,
+                                      0x00FF00FF00FF00FFull, 0x0F0F0F0F0F0F0F0Full,
+                                      0x3333333333333333ull, 0x5555555555555555ull};
+#pragma unroll
+  for (int st = 0; st < 6; ++st) {
+    const int s = 32 >> st;
+    const uint64_t mask = kBlockMask[st];
+    const uint64_t p = __shfl_xor(m, s);
+    // the lower lane takes the partner's low block into its high half, the
+    // upper lane the partner's high block into its low half
+    const uint64_t t_lo = (((m >> s) ^ p) & mask) << s;
+    const uint64_t t_hi = ((p >> s) ^ m) & mask;
+    m ^= (lane & s) ? t_hi : t_lo;
+  }
+  return m;
+}
+
 // ---- agent-scope atomics (visible across all XCDs of the device) ----------
 __device__ __forceinline__ uint64_t ld_acquire(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);

@@ -177,11 +177,7 @@ __device__ __forceinline__ void ballots(const TileSlots<KMAX>& s, int P, int wav
     for (int k = 0; k < KMAX; ++k)
       if (s.bin[k] >= w0 && s.bin[k] < w0 + kWave) m |= uint64_t(1) << (s.bin[k] - w0);
     const int nwin = min(kWave, P - w0);
-    uint64_t mine = 0;
-    for (int j = 0; j < nwin; ++j) {
-      const uint64_t b = ballot((m >> j) & 1u);
-      if (lane == j) mine = b;
-    }
+    const uint64_t mine = wave_bin_ballots(m);
     if (lane < nwin) s_bal[wave * P + w0 + lane] = mine;
   }
 }

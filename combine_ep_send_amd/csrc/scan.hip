@@ -100,10 +100,8 @@ __global__ __launch_bounds__(kBlock) void counts_kernel(CountArgs a) {
         for (int j = 0; j < nwin; ++j) row[j] = uint8_t((m >> j) & 1u);
       }
     }
-    for (int j = 0; j < nwin; ++j) {
-      const uint64_t b = ballot((m >> j) & 1u);
-      if (b != 0 && lane == 0) atomicAdd(&s_hist[w0 + j], int(__popcll(b)));
-    }
+    const uint64_t col = wave_bin_ballots(m);
+    if (lane < nwin && col != 0) atomicAdd(&s_hist[w0 + lane], int(__popcll(col)));
   }
   if (want_e) {
 #pragma unroll
@@ -210,11 +208,7 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanArgs a) {
     for (int k = 0; k < KMAX; ++k)
       if (bin[k] >= w0 && bin[k] < w0 + kWave) m |= uint64_t(1) << (bin[k] - w0);
     const int nwin = min(kWave, nb - w0);
-    uint64_t mine = 0;
-    for (int j = 0; j < nwin; ++j) {
-      const uint64_t b = ballot((m >> j) & 1u);
-      if (lane == j) mine = b;
-    }
+    const uint64_t mine = wave_bin_ballots(m);
     if (lane < nwin) s_bal[wave * nb + w0 + lane] = mine;
   }
   // Segment starts of the send layout: exclusive scan of send_counts.
