@@ -38,19 +38,14 @@ int check_hidden(int H, bool fp8) {
 
 // Control header, published rows, per-group prefixes and bin totals of the
 // fused launch, laid out as ep_*_workspace_bytes sizes them.
-void set_fused_workspace(FusedArgs& a, void* ws, int64_t tiles, int64_t bins, int64_t row_words,
+void set_fused_workspace(FusedArgs& a, void* ws, int64_t bins, int64_t row_words,
                          int64_t groups) {
-  const int64_t gcap = tiles < kMaxFusedGroups ? tiles : kMaxFusedGroups;
+  const int64_t gcap = a.tiles < kMaxFusedGroups ? a.tiles : kMaxFusedGroups;
   a.ctrl = static_cast<uint32_t*>(ws);
   a.rows = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kWsHeaderBytes);
   a.pref = a.rows + gcap * row_words;
   a.tots = a.pref + gcap * bins;
-  a.two_pass = fused_two_pass(groups, bins);
-}
-
-int64_t fused_tiles(int64_t T) {
-  const int64_t t = (T + 255) / 256;   // tiles of 256 tokens
-  return t > 0 ? t : 1;
+  a.two_pass = fused_two_pass(groups, bins, a.waves);
 }
 
 // Compute units of the current device (cached per device id).
@@ -65,6 +60,28 @@ int device_cus() {
   if (dev < 64) cached[dev] = n;
   return n;
 }
+
+// Shape of a fused launch over T rows: tiles, tiles per workgroup (at most
+// one workgroup per compute unit, each a contiguous run of tiles), and
+// whether its LDS share stays within kSmemLimit.
+constexpr size_t kSmemLimit = 64 * 1024;
+struct FusedShape {
+  int waves;
+  int64_t tiles, per, groups;
+  bool fits;
+};
+FusedShape fused_shape(int64_t T, int bins, int E) {
+  FusedShape f{};
+  f.waves = fused_waves(T);
+  f.tiles = fused_tiles(T);
+  int64_t gmax = device_cus();
+  if (gmax > kMaxFusedGroups) gmax = kMaxFusedGroups;
+  f.per = (f.tiles + gmax - 1) / gmax;
+  f.groups = (f.tiles + f.per - 1) / f.per;
+  f.fits = fused_smem_bytes(bins, E, int(f.per), f.waves) <= kSmemLimit;
+  return f;
+}
+
 
 }  // namespace
 
@@ -184,7 +201,7 @@ size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
                                           int num_local_experts) {
   if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1) return 0;
   const int64_t nh = int64_t(num_ranks) + int64_t(num_ranks) * num_local_experts + 1;
-  return fused_ws_bytes(fused_tiles(num_tokens), num_ranks, nh);
+  return fused_ws_bytes(num_tokens, num_ranks, nh);
 }
 
 int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64_t num_tokens,
@@ -212,18 +229,9 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
       workspace_bytes < ep_dispatch_layout_workspace_bytes(num_tokens, num_ranks,
                                                            num_local_experts))
     return EP_ERR_WORKSPACE;
-  // Groups: one per compute unit at most, each a contiguous run of tiles.
-  const int64_t tiles = fused_tiles(num_tokens);
   const int E = num_ranks * num_local_experts;
-  constexpr size_t kSmemLimit = 64 * 1024;
-  if (fused_smem_bytes(num_ranks, E, int((tiles + kMaxFusedGroups - 1) / kMaxFusedGroups)) >
-      kSmemLimit)
-    return EP_ERR_UNSUPPORTED;
-  int64_t gmax = device_cus();
-  if (gmax > kMaxFusedGroups) gmax = kMaxFusedGroups;
-  const int64_t per = (tiles + gmax - 1) / gmax;
-  const int64_t groups = (tiles + per - 1) / per;
-  if (fused_smem_bytes(num_ranks, E, int(per)) > kSmemLimit) return EP_ERR_UNSUPPORTED;
+  const FusedShape sh = fused_shape(num_tokens, num_ranks, E);
+  if (!sh.fits) return EP_ERR_UNSUPPORTED;
 
   FusedArgs a{};
   a.topk_idx = topk_idx;
@@ -246,15 +254,16 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
   a.token_row = token_row;
   a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
   a.vec_in = (num_topk % 4) == 0 && aligned(topk_idx, 16) && aligned(topk_weights, 16);
-  set_fused_workspace(a, workspace, tiles, num_ranks, int64_t(num_ranks) + E + 1, groups);
-  a.tiles = tiles;
-  a.tiles_per_group = int(per);
-  return launch_status(launch_dispatch_layout(a, unsigned(groups), stream));
+  a.tiles = sh.tiles;
+  a.tiles_per_group = int(sh.per);
+  a.waves = sh.waves;
+  set_fused_workspace(a, workspace, num_ranks, int64_t(num_ranks) + E + 1, sh.groups);
+  return launch_status(launch_dispatch_layout(a, unsigned(sh.groups), stream));
 }
 
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins) {
   if (num_rows < 0 || num_bins < 1) return 0;
-  return fused_ws_bytes(fused_tiles(num_rows), num_bins, int64_t(num_bins) + 1);
+  return fused_ws_bytes(num_rows, num_bins, int64_t(num_bins) + 1);
 }
 
 int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const float* recv_w,
@@ -284,16 +293,8 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   if (!workspace || !aligned(workspace, 256) ||
       workspace_bytes < ep_regroup_workspace_bytes(num_rows, bins))
     return EP_ERR_WORKSPACE;
-  const int64_t tiles = fused_tiles(num_rows);
-  constexpr size_t kSmemLimit = 64 * 1024;
-  if (fused_smem_bytes(bins, 0, int((tiles + kMaxFusedGroups - 1) / kMaxFusedGroups)) >
-      kSmemLimit)
-    return EP_ERR_UNSUPPORTED;
-  int64_t gmax = device_cus();
-  if (gmax > kMaxFusedGroups) gmax = kMaxFusedGroups;
-  const int64_t per = (tiles + gmax - 1) / gmax;
-  const int64_t groups = (tiles + per - 1) / per;
-  if (fused_smem_bytes(bins, 0, int(per)) > kSmemLimit) return EP_ERR_UNSUPPORTED;
+  const FusedShape sh = fused_shape(num_rows, bins, 0);
+  if (!sh.fits) return EP_ERR_UNSUPPORTED;
 
   // 1. one launch: counts per local expert, aligned offsets, row_map, the
   //    source row and weight of every regrouped row
@@ -309,14 +310,15 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   a.send_counts = tokens_per_expert;
   a.send_token_idx = perm_src;
   a.token_row = row_map;
-  set_fused_workspace(a, workspace, tiles, bins, int64_t(bins) + 1, groups);
-  a.tiles = tiles;
-  a.tiles_per_group = int(per);
+  a.tiles = sh.tiles;
+  a.tiles_per_group = int(sh.per);
+  a.waves = sh.waves;
+  set_fused_workspace(a, workspace, bins, int64_t(bins) + 1, sh.groups);
   a.ids32 = recv_idx;
   a.align = align;
   a.offsets = expert_offsets;
   a.perm_w = perm_w;
-  if (launch_regroup_layout(a, unsigned(groups), stream) != hipSuccess) return EP_ERR_LAUNCH;
+  if (launch_regroup_layout(a, unsigned(sh.groups), stream) != hipSuccess) return EP_ERR_LAUNCH;
 
   // 2. padding rows; 3. the received rows, token-major through row_map
   RegroupPadArgs z{};

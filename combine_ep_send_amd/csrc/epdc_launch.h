@@ -95,8 +95,9 @@ struct FusedArgs {
   uint32_t* pref;                // [groups, P] per-group exclusive prefixes (two-pass scan)
   uint32_t* tots;                // [P] bin totals (two-pass scan)
   bool two_pass;                 // scan the rows bin by bin, with a second barrier
-  int64_t tiles;                 // tiles of 256 tokens (>= 1)
+  int64_t tiles;                 // tiles of waves*64 tokens (>= 1)
   int tiles_per_group;
+  int waves;                     // waves per workgroup: 1, 2 or 4 (one token per thread)
   // regroup by local expert (P = E_local bins, E = 0)
   const int32_t* ids32;          // [R,K] local expert ids, -1 = not local
   const int32_t* row_group;      // [R] receive buffer of each row, or null (P = groups*E_local)
@@ -109,17 +110,33 @@ struct FusedArgs {
 constexpr int kMaxFusedGroups = 256;
 // Bins one workgroup scans in the two-pass form (at most).
 constexpr int kMaxTwoPassBins = 8;
-// Workspace of the fused launch: header, rows, prefixes, totals.
-inline size_t fused_ws_bytes(int64_t tiles, int64_t bins, int64_t row_words) {
+// Tiles of the fused launch: one token per thread of a workgroup of 1, 2 or
+// 4 waves, chosen so that about 64 tiles cover the input (small inputs then
+// spread over more compute units; large ones keep 256-token tiles).
+inline int fused_waves(int64_t T) {
+  const int64_t w = (T + 64 * 64 - 1) / (64 * 64);
+  return w <= 1 ? 1 : (w <= 2 ? 2 : 4);
+}
+inline int64_t fused_tiles(int64_t T) {
+  const int64_t tile = int64_t(fused_waves(T)) * 64;
+  const int64_t t = (T + tile - 1) / tile;
+  return t > 0 ? t : 1;
+}
+// Workspace of the fused launch over T rows: header, rows, prefixes, totals.
+inline size_t fused_ws_bytes(int64_t T, int64_t bins, int64_t row_words) {
+  const int64_t tiles = fused_tiles(T);
   const int64_t g = tiles < kMaxFusedGroups ? tiles : kMaxFusedGroups;
   return kWsHeaderBytes + size_t(g) * size_t(row_words) * 4u + size_t(g) * size_t(bins) * 4u +
          size_t(bins) * 4u;
 }
-// Whether a launch of `groups` workgroups over `bins` bins takes the two-pass scan.
-inline bool fused_two_pass(int64_t groups, int64_t bins) {
-  return groups * bins > 8 * 256 && (bins + groups - 1) / groups <= kMaxTwoPassBins;
+// Whether a launch of `groups` workgroups of `waves` waves over `bins` bins
+// takes the two-pass scan (the single pass would need more than 8 loads per
+// thread, and no workgroup has more than kMaxTwoPassBins bins to scan).
+inline bool fused_two_pass(int64_t groups, int64_t bins, int waves) {
+  return groups * bins > 8 * 64 * int64_t(waves) &&
+         (bins + groups - 1) / groups <= kMaxTwoPassBins;
 }
-size_t fused_smem_bytes(int P, int E, int tiles_per_group);
+size_t fused_smem_bytes(int P, int E, int tiles_per_group, int waves);
 hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
 hipError_t launch_regroup_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
 

@@ -4,7 +4,9 @@
 // "uccl_ep.buffer": Buffer.get_dispatch_layout.  Same outputs as the two
 // separate calls, computed as reduce-then-scan with one grid-wide barrier:
 //
-//  1. Each workgroup owns a contiguous run of tiles (256 tokens each).  It
+//  1. Each workgroup owns a contiguous run of tiles (one token per thread:
+//     64, 128 or 256 tokens, so that small inputs still spread over many
+//     compute units).  It
 //     decodes them (dest, is_in_rank), counts every tile's tokens per
 //     destination with per-wave ballots, histograms experts in LDS, and
 //     publishes its totals per destination / expert as one row.
@@ -65,6 +67,7 @@ __device__ __forceinline__ void grid_sync(uint32_t* ctrl, int G, uint32_t gen, u
 
 // Exclusive prefix sum over the workgroup's threads (thread order); `total`
 // receives the sum of all.  s_scan holds one word per wave.
+template <int NW>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_scan,
                                                          uint32_t& total) {
   const int lane = lane_id();
@@ -80,7 +83,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   uint32_t before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t t = s_scan[w];
     if (w < wave) before += t;
     total += t;
@@ -182,19 +185,20 @@ __device__ __forceinline__ void ballots(const TileSlots<KMAX>& s, int P, int wav
   }
 }
 
-template <int MODE, int KMAX>
-__global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
+template <int MODE, int KMAX, int NW>
+__global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a) {
+  constexpr int BS = NW * kWave;        // threads per workgroup = tokens per tile
   extern __shared__ __align__(16) unsigned char smem[];
   const int P = a.P;
   const int nh = a.P + a.E + 1;                 // published row: P dests, E experts, bad
   uint64_t* s_bal = reinterpret_cast<uint64_t*>(smem);                        // [4][P]
-  int32_t* s_woff = reinterpret_cast<int32_t*>(s_bal + kWavesPerBlock * P);   // [4][P]
-  int32_t* s_tcnt = s_woff + kWavesPerBlock * P;                             // [tpw][P]
+  int32_t* s_woff = reinterpret_cast<int32_t*>(s_bal + NW * P);             // [NW][P]
+  int32_t* s_tcnt = s_woff + NW * P;                                         // [tpw][P]
   int32_t* s_hist = s_tcnt + a.tiles_per_group * P;                          // [nh]
   int32_t* s_tot = s_hist + nh;                                              // [P]
   int32_t* s_base = s_tot + P;                                               // [P]
   __shared__ int32_t s_bad;
-  __shared__ uint32_t s_scan[kWavesPerBlock];
+  __shared__ uint32_t s_scan[NW];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -211,13 +215,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   // its round trip overlaps the decode.
   const uint32_t gen = tid == 0 ? ld_relaxed(&a.ctrl[kCtrlEpoch]) : 0u;
   if (tid == 0) s_bad = 0;
-  for (int i = tid; i < nh; i += kBlock) s_hist[i] = 0;
+  for (int i = tid; i < nh; i += BS) s_hist[i] = 0;
   __syncthreads();
 
   // ---- 1. decode, count, publish ------------------------------------------
   TileSlots<KMAX> sl;
   for (int j = 0; j < my_tiles; ++j) {
-    const int64_t t = (tile0 + j) * kTile + tid;
+    const int64_t t = (tile0 + j) * BS + tid;
     const bool valid = t < a.T;
     decode<MODE, KMAX>(a, t, valid, sl);
     if (MODE == kFusedSend && valid) {
@@ -248,17 +252,17 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
     if (sl.bad) atomicAdd(&s_hist[nh - 1], sl.bad);
     ballots<KMAX>(sl, P, wave, lane, s_bal);
     __syncthreads();
-    for (int b = tid; b < P; b += kBlock) {
+    for (int b = tid; b < P; b += BS) {
       int cnt = 0;
 #pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) cnt += int(__popcll(s_bal[w * P + b]));
+      for (int w = 0; w < NW; ++w) cnt += int(__popcll(s_bal[w * P + b]));
       s_tcnt[j * P + b] = cnt;
       s_hist[b] += cnt;
     }
     __syncthreads();
   }
   uint32_t* row_out = a.rows + int64_t(g) * nh;
-  for (int i = tid; i < nh; i += kBlock) st_relaxed(row_out + i, uint32_t(s_hist[i]));
+  for (int i = tid; i < nh; i += BS) st_relaxed(row_out + i, uint32_t(s_hist[i]));
 
   // ---- 2. grid barrier --------------------------------------------------------
   grid_sync(a.ctrl, G, gen, 1, !a.two_pass);
@@ -270,43 +274,58 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   const int e1 = min(a.E, e0 + per_g);
   const int ne = want_e && e1 > e0 ? e1 - e0 : 0;
   int32_t* s_etot = s_hist;            // reuse (the row is published): [ne] expert totals
-  for (int b = tid; b < P; b += kBlock) {
+  for (int b = tid; b < P; b += BS) {
     s_tot[b] = 0;
     s_base[b] = 0;
   }
-  for (int i = tid; i < ne; i += kBlock) s_etot[i] = 0;
+  for (int i = tid; i < ne; i += BS) s_etot[i] = 0;
   __syncthreads();
   if (a.two_pass) {
     // Many groups and bins: every workgroup reading all lower rows would
     // take G*P loads each.  Instead workgroup g scans a slice of the bins
-    // over the groups (thread i holds group i's count; one load each), and
-    // publishes each group's exclusive prefix and the bin's total; after a
-    // second barrier every workgroup reads its own prefixes and the totals
-    // (P loads each).
+    // over the groups (thread i holds the counts of groups [i*q, i*q + q),
+    // all loads in flight together), and publishes each group's exclusive
+    // prefix and the bin's total; after a second barrier every workgroup
+    // reads its own prefixes and the totals (P loads each).
+    constexpr int kQ = kMaxFusedGroups / BS;       // groups per thread (at most)
+    const int q = (G + BS - 1) / BS;
     const int per_b = (P + G - 1) / G;
     const int b0 = g * per_b;
-    uint32_t v[kMaxTwoPassBins];
+    uint32_t v[kMaxTwoPassBins][kQ];
 #pragma unroll
     for (int u = 0; u < kMaxTwoPassBins; ++u) {
       const int b = b0 + u;
-      v[u] = (u < per_b && b < P && tid < G) ? ld_relaxed(a.rows + int64_t(tid) * nh + b) : 0u;
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int grp = tid * q + i;
+        v[u][i] = (u < per_b && b < P && i < q && grp < G)
+                      ? ld_relaxed(a.rows + int64_t(grp) * nh + b) : 0u;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kMaxTwoPassBins; ++u) {
       const int b = b0 + u;
       if (u >= per_b || b >= P) break;             // uniform across the workgroup
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) mine += v[u][i];
       uint32_t total = 0;
-      const uint32_t ex = block_exclusive_scan(v[u], s_scan, total);
-      if (tid < G) st_relaxed(a.pref + int64_t(tid) * P + b, ex);
+      uint32_t ex = block_exclusive_scan<NW>(mine, s_scan, total);
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int grp = tid * q + i;
+        if (i < q && grp < G) st_relaxed(a.pref + int64_t(grp) * P + b, ex);
+        ex += v[u][i];
+      }
       if (tid == 0) st_relaxed(a.tots + b, total);
     }
     // the expert slice, as in the single pass
-    for (int i0 = tid; i0 < G * ne; i0 += kBlock * 8) {
+    for (int i0 = tid; i0 < G * ne; i0 += BS * 8) {
       uint32_t vx[8];
       int ex[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kBlock;
+        const int i = i0 + u * BS;
         vx[u] = 0u;
         ex[u] = 0;
         if (i < G * ne) {
@@ -319,7 +338,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
         if (vx[u]) atomicAdd(&s_etot[ex[u]], int(vx[u]));
     }
     grid_sync(a.ctrl, G, gen, 2, true);
-    for (int b = tid; b < P; b += kBlock) {
+    for (int b = tid; b < P; b += BS) {
       s_base[b] = int(ld_relaxed(a.pref + int64_t(g) * P + b));
       s_tot[b] = int(ld_relaxed(a.tots + b));
     }
@@ -331,12 +350,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
     const int nd = G * P;
     const int nx = G * ne;
     const int n = nd > nx ? nd : nx;
-    for (int i0 = tid; i0 < n; i0 += kBlock * 8) {
+    for (int i0 = tid; i0 < n; i0 += BS * 8) {
       uint32_t vd[8], vx[8];
       int gd[8], bd[8], ex[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kBlock;
+        const int i = i0 + u * BS;
         vd[u] = 0u;
         vx[u] = 0u;
         gd[u] = 0;
@@ -365,15 +384,15 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
     }
   }
   if (g == 0 && a.diag) {
-    for (int grp = tid; grp < G; grp += kBlock) {
+    for (int grp = tid; grp < G; grp += BS) {
       const uint32_t v = ld_relaxed(a.rows + int64_t(grp) * nh + nh - 1);
       if (v) atomicAdd(&s_bad, int(v));
     }
   }
   __syncthreads();
-  for (int i = tid; i < ne; i += kBlock) a.tokens_per_expert[e0 + i] = s_etot[i];
+  for (int i = tid; i < ne; i += BS) a.tokens_per_expert[e0 + i] = s_etot[i];
   if (g == 0) {
-    for (int b = tid; b < P; b += kBlock) a.send_counts[b] = s_tot[b];
+    for (int b = tid; b < P; b += BS) a.send_counts[b] = s_tot[b];
     if (tid == 0 && a.diag) a.diag[0] = s_bad;
   }
   // Segment starts (exclusive scan of the totals, each rounded up to the
@@ -403,17 +422,17 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
   // ---- 4. rows and scatter ------------------------------------------------------
   const uint64_t lt = lanemask_lt();
   for (int j = 0; j < my_tiles; ++j) {
-    const int64_t t = (tile0 + j) * kTile + tid;
+    const int64_t t = (tile0 + j) * BS + tid;
     const bool valid = t < a.T;
     if (my_tiles > 1) {       // a single tile's slots are still in registers
       decode<MODE, KMAX>(a, t, valid, sl);
       ballots<KMAX>(sl, P, wave, lane, s_bal);
     }
     __syncthreads();
-    for (int b = tid; b < P; b += kBlock) {
+    for (int b = tid; b < P; b += BS) {
       int run = s_base[b];
 #pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) {
+      for (int w = 0; w < NW; ++w) {
         s_woff[w * P + b] = run;
         run += int(__popcll(s_bal[w * P + b]));
       }
@@ -482,26 +501,36 @@ __global__ __launch_bounds__(kBlock) void dispatch_layout_kernel(FusedArgs a) {
       }
     }
     __syncthreads();
-    for (int b = tid; b < P; b += kBlock) s_base[b] += s_tcnt[j * P + b];
+    for (int b = tid; b < P; b += BS) s_base[b] += s_tcnt[j * P + b];
   }
 }
 
 }  // namespace
 
-size_t fused_smem_bytes(int P, int E, int tiles_per_group) {
-  return size_t(P) * (kWavesPerBlock * 8 + kWavesPerBlock * 4 + 2 * 4) +
+size_t fused_smem_bytes(int P, int E, int tiles_per_group, int waves) {
+  return size_t(P) * (size_t(waves) * 8 + size_t(waves) * 4 + 2 * 4) +
          size_t(tiles_per_group) * P * 4 + size_t(P + E + 1) * 4;
+}
+
+template <int MODE, int NW>
+void launch_fused_nw(const FusedArgs& a, unsigned groups, size_t smem, hipStream_t s) {
+  if (a.K <= 4)
+    dispatch_layout_kernel<MODE, 4, NW><<<groups, NW * kWave, smem, s>>>(a);
+  else if (a.K <= 8)
+    dispatch_layout_kernel<MODE, 8, NW><<<groups, NW * kWave, smem, s>>>(a);
+  else
+    dispatch_layout_kernel<MODE, 16, NW><<<groups, NW * kWave, smem, s>>>(a);
 }
 
 template <int MODE>
 hipError_t launch_fused(const FusedArgs& a, unsigned groups, hipStream_t s) {
-  const size_t smem = fused_smem_bytes(a.P, a.E, a.tiles_per_group);
-  if (a.K <= 4)
-    dispatch_layout_kernel<MODE, 4><<<groups, kBlock, smem, s>>>(a);
-  else if (a.K <= 8)
-    dispatch_layout_kernel<MODE, 8><<<groups, kBlock, smem, s>>>(a);
+  const size_t smem = fused_smem_bytes(a.P, a.E, a.tiles_per_group, a.waves);
+  if (a.waves == 1)
+    launch_fused_nw<MODE, 1>(a, groups, smem, s);
+  else if (a.waves == 2)
+    launch_fused_nw<MODE, 2>(a, groups, smem, s);
   else
-    dispatch_layout_kernel<MODE, 16><<<groups, kBlock, smem, s>>>(a);
+    launch_fused_nw<MODE, 4>(a, groups, smem, s);
   return hipGetLastError();
 }
 

@@ -190,7 +190,8 @@ int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights,
  * words: [0] barrier arrivals, [2] barrier generation, [3] error flags: bit 0
  * = a barrier wait gave up) followed by G rows of P + E + 1 uint32 (one per
  * workgroup), G rows of P uint32 (per-workgroup prefixes) and P uint32
- * (totals), G = min(ceil(T/256), 256).  Zero-filled once before first use;
+ * (totals), G = min(ceil(T/tile), 256) with tiles of 64 tokens for T <= 4096,
+ * 128 for T <= 8192, 256 above.  Zero-filled once before first use;
  * every call leaves it ready for the next; calls that may overlap in time
  * must use different workspaces.
  */
@@ -236,7 +237,7 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights,
  * Bytes of workspace ep_regroup_by_expert needs for R received rows and
  * num_bins = num_groups * E_local bins: a 256-byte header (as
  * ep_dispatch_layout's), G rows of num_bins + 1 uint32, G rows of num_bins
- * uint32 and num_bins uint32, G = min(ceil(R/256), 256).  Same zero-once /
+ * uint32 and num_bins uint32, G as for ep_dispatch_layout with T = R.  Same zero-once /
  * no-overlap rules.
  */
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins);

@@ -129,12 +129,13 @@ def test_fused_layout_workspace_and_arguments():
     assert call(ws=A8) == _lib.EP_ERR_WORKSPACE
     assert call(ws_bytes=64) == _lib.EP_ERR_WORKSPACE
     # LDS share over 64 KiB (1024 destinations x 8 experts): use the two calls
-    assert call(P=1024, El=8) == _lib.EP_ERR_UNSUPPORTED
+    assert call(T=20000, P=1024, El=8) == _lib.EP_ERR_UNSUPPORTED
 
 
 def test_regroup_workspace_and_arguments():
     L = _lib.lib()
-    assert L.ep_regroup_workspace_bytes(1000, 8) == 256 + 4 * (8 + 1) * 4 + 4 * 8 * 4 + 8 * 4
+    # 1000 rows: 64-row tiles, 16 workgroups
+    assert L.ep_regroup_workspace_bytes(1000, 8) == 256 + 16 * (8 + 1) * 4 + 16 * 8 * 4 + 8 * 4
     assert L.ep_regroup_workspace_bytes(0, 8) == 256 + 1 * 9 * 4 + 8 * 4 + 8 * 4
     assert L.ep_regroup_workspace_bytes(10, 0) == 0
     f = L.ep_regroup_by_expert

@@ -154,12 +154,15 @@ def test_fused_bad_ids_and_empty():
 
 def _barriers(T, P):
     """Grid barriers one fused call takes: two when its groups x bins table
-    is scanned bin by bin (more than 2048 entries, at most 8 bins per group)."""
-    tiles = max(1, -(-T // 256))
+    is scanned bin by bin (more than 8 entries per thread of a workgroup, at
+    most 8 bins per group).  Tiles are 64 tokens up to T = 4096, 128 up to
+    8192, 256 above (one token per thread)."""
+    waves = 1 if T <= 4096 else (2 if T <= 8192 else 4)
+    tiles = max(1, -(-T // (64 * waves)))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     per = -(-tiles // min(cus, 256))
     groups = -(-tiles // per)
-    return 2 if groups * P > 2048 and -(-P // groups) <= 8 else 1
+    return 2 if groups * P > 8 * 64 * waves and -(-P // groups) <= 8 else 1
 
 
 def test_fused_workspace_reused_across_calls_and_sizes():
