@@ -254,6 +254,8 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
   a.token_row = token_row;
   a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
   a.vec_in = (num_topk % 4) == 0 && aligned(topk_idx, 16) && aligned(topk_weights, 16);
+  a.vec_out = (num_topk % 4) == 0 && aligned(dest, 16) && aligned(token_row, 16);
+  a.vec_iir = (num_ranks % 16) == 0 && aligned(is_in_rank, 16);
   a.tiles = sh.tiles;
   a.tiles_per_group = int(sh.per);
   a.waves = sh.waves;
@@ -310,6 +312,7 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   a.send_counts = tokens_per_expert;
   a.send_token_idx = perm_src;
   a.token_row = row_map;
+  a.vec_out = (num_topk % 4) == 0 && aligned(row_map, 16);
   a.tiles = sh.tiles;
   a.tiles_per_group = int(sh.per);
   a.waves = sh.waves;

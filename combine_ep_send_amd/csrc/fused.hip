@@ -170,6 +170,22 @@ __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid
   }
 }
 
+// One token's K int32 entries: 16-byte stores when the row is whole (K ==
+// KMAX, a multiple of 4) and aligned, else one word per slot.
+template <int KMAX>
+__device__ __forceinline__ void store_row(int32_t* dst, const int (&v)[KMAX], int K, bool vec) {
+  if (vec && K == KMAX && (KMAX % 4) == 0) {
+#pragma unroll
+    for (int q = 0; q < KMAX / 4; ++q)
+      reinterpret_cast<u32x4*>(dst)[q] = u32x4{uint32_t(v[4 * q]), uint32_t(v[4 * q + 1]),
+                                               uint32_t(v[4 * q + 2]), uint32_t(v[4 * q + 3])};
+  } else {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (k < K) dst[k] = v[k];
+  }
+}
+
 // Per-wave ballots of every destination for one tile: s_bal[wave*P + b].
 template <int KMAX>
 __device__ __forceinline__ void ballots(const TileSlots<KMAX>& s, int P, int wave, int lane,
@@ -225,22 +241,24 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
     const bool valid = t < a.T;
     decode<MODE, KMAX>(a, t, valid, sl);
     if (MODE == kFusedSend && valid) {
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k)
-        if (k < a.K) a.dest[t * a.K + k] = sl.bin[k];
-      // membership row, 4 destinations per 32-bit store when P % 4 == 0
+      store_row<KMAX>(a.dest + t * a.K, sl.bin, a.K, a.vec_out);
+      // membership row: 16 destinations per 16-byte store when the rows
+      // allow it, else 4 per 32-bit store (P % 4 == 0) or bytes
       uint8_t* row = a.is_in_rank + t * P;
-      for (int p0 = 0; p0 < P; p0 += 4) {
-        uint32_t word = 0;
+      const int step = a.vec_iir ? 16 : 4;
+      for (int p0 = 0; p0 < P; p0 += step) {
+        uint32_t word[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
           const int d = sl.bin[k] - p0;
-          if (d >= 0 && d < 4) word |= 1u << (8 * d);
+          if (d >= 0 && d < step) word[d >> 2] |= 1u << (8 * (d & 3));
         }
-        if ((P & 3) == 0) {
-          *reinterpret_cast<uint32_t*>(row + p0) = word;
+        if (a.vec_iir) {
+          *reinterpret_cast<u32x4*>(row + p0) = u32x4{word[0], word[1], word[2], word[3]};
+        } else if ((P & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(row + p0) = word[0];
         } else {
-          for (int q = 0; q < 4 && p0 + q < P; ++q) row[p0 + q] = uint8_t((word >> (8 * q)) & 1u);
+          for (int q = 0; q < 4 && p0 + q < P; ++q) row[p0 + q] = uint8_t((word[0] >> (8 * q)) & 1u);
         }
       }
     }
@@ -448,11 +466,7 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
         if (n < a.capacity) rowk[k] = int32_t(n);
       }
     }
-    if (valid) {
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k)
-        if (k < a.K) a.token_row[t * a.K + k] = rowk[k];
-    }
+    if (valid) store_row<KMAX>(a.token_row + t * a.K, rowk, a.K, a.vec_out);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       bool first = sl.bin[k] >= 0 && rowk[k] >= 0;
