@@ -374,6 +374,7 @@ int ep_dispatch_permute(const void* x, int64_t num_tokens, int hidden, const int
   a.out_scale = fp8 ? send_scale : nullptr;
   a.scale_fmt = kScaleF32;
   a.scale_block_rows = 0;
+  a.capped = true;
   return launch_status(fp8 ? launch_permute_fp8(a, stream) : launch_permute_bf16(a, stream));
 }
 

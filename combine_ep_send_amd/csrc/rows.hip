@@ -475,8 +475,11 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 // both.  With fewer rows in flight the scattered row stores stream better:
 // on the 16k-token scatter the bf16 permute measured 329 us against 351 us
 // at full occupancy, the fp8 permute 109 against 113 us on an 8k-token
-// chunk (caps of 7, 9 or more workgroups were slower).  The sparse
-// expert-batched fills, whose workgroups mostly exit at once, run uncapped.
+// chunk (caps of 7, 9 or more workgroups were slower).  Only the send
+// layout's permutes (about 7 rows per token) are capped: the regroup's copy
+// (about one row per received row) measured slower capped (903 against
+// 728 us), and the sparse expert-batched fills' workgroups mostly exit at
+// once.
 constexpr unsigned kPermuteLdsCap = 18 * 1024;
 constexpr unsigned kFp8PermuteLdsCap = 10 * 1024;
 
@@ -513,7 +516,8 @@ void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
     if (a.sparse)
       permute_bf16_kernel<KMAX, 1, false><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
     else
-      permute_bf16_kernel<KMAX, 1, true><<<g, kPermuteBlock, kPermuteLdsCap, s>>>(a, nchunks, i0);
+      permute_bf16_kernel<KMAX, 1, true><<<g, kPermuteBlock, a.capped ? kPermuteLdsCap : 0u, s>>>(
+          a, nchunks, i0);
   });
 }
 
@@ -523,8 +527,8 @@ void launch_permute_fp8_p(const RowArgs& a, Split sp, hipStream_t s) {
     if (a.sparse)
       permute_fp8_kernel<KMAX, IT, SFMT, false><<<g, kWave, 0, s>>>(a, sp.nchunks, i0);
     else
-      permute_fp8_kernel<KMAX, IT, SFMT, true><<<g, kWave, kFp8PermuteLdsCap, s>>>(a, sp.nchunks,
-                                                                                   i0);
+      permute_fp8_kernel<KMAX, IT, SFMT, true><<<g, kWave, a.capped ? kFp8PermuteLdsCap : 0u, s>>>(
+          a, sp.nchunks, i0);
   });
 }
 
