@@ -498,6 +498,7 @@ def cpu_baseline(s, budget_tokens):
         "seconds": round(dt, 3),
         "cores": 1,
         "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"first {T} tokens of the {s.name} workload (same generator and seed), "
                   f"all phases, numpy single-threaded" +
@@ -625,6 +626,7 @@ def main():
         ev1.record(main_stream)
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / args.steps
+        step_ms = [ms]
     else:
         # Each step between its own events, the cache-clearing write before it.
         evs = []
@@ -637,7 +639,8 @@ def main():
             e1.record(main_stream)
             evs.append((e0, e1))
         torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        step_ms = [a.elapsed_time(b) for a, b in evs]
+        ms = float(np.mean(step_ms))
     wall = time.perf_counter() - w0
     log(f"[bench] {args.steps} timed steps: {ms:.4f} ms/step (events), "
         f"{1000 * wall / args.steps:.4f} ms/step (wall)")
@@ -668,6 +671,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_median": round(float(np.median(step_ms)), 5),
+        "ms_per_step_min": round(float(np.min(step_ms)), 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
