@@ -556,7 +556,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU exchange in this build)", file=sys.stderr)
+              "(the library has no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import torch
