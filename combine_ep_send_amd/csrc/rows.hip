@@ -102,37 +102,11 @@ __global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, 
 }
 
 // ---------------------------------------------------------------------------
-// Expert-batched fill (bf16): most tokens have no local expert, so a
-// workgroup takes a whole row (up to kMaxRowBlock pieces, one per thread),
-// looks its rows up first and leaves at once when there are none: a quarter
-// as many workgroups as the chunked permute, most of them gone after one
-// scalar round trip.
-// ---------------------------------------------------------------------------
-template <int KMAX>
-__global__ __launch_bounds__(kMaxRowBlock) void batched_fill_bf16_kernel(RowArgs a, int nchunks,
-                                                                         int64_t item0) {
-  const int H8 = a.H >> 3;
-  const int64_t item = item0 + blockIdx.x;
-  const int64_t t = udiv(item, nchunks);
-  const int j = int(item - t * nchunks) * int(blockDim.x) + int(threadIdx.x);
-  int32_t rows[KMAX];
-  bool use[KMAX];
-  if (token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use) == 0 || j >= H8) return;
-  const u32x4 v = ld_stream(static_cast<const u32x4*>(a.x) + t * H8 + j);
-  u32x4* dst = static_cast<u32x4*>(a.out);
-#pragma unroll
-  for (int k = 0; k < KMAX; ++k)
-    if (use[k]) st_stream(dst + int64_t(rows[k]) * H8 + j, v);
-}
-
-// ---------------------------------------------------------------------------
 // fp8 quantize-on-dispatch.  A lane owns 16 consecutive channels (32 bytes
 // of bf16 in, 16 bytes of e4m3 out); 8 lanes form one 128-channel group and
 // reduce its amax with three xor shuffles.  One wave per (token, chunk of
 // 64*IT 16-channel pieces); the chunk is quantized once and stored to every
-// row of the token.  The expert-batched fill (LOAD_FIRST = false) gives a
-// workgroup several waves, up to a whole row, for the reason given at the
-// bf16 fill.
+// row of the token.
 //
 // Scales: fl32(amax/448) (SFMT kScaleF32); the smallest power of two at or
 // above it (kScalePow2); or that power's UE8M0 byte, exponent + 127 and at
@@ -166,11 +140,9 @@ __device__ __forceinline__ float pow2_ceil(float s) {
 }
 
 template <int KMAX, int IT, int SFMT, bool LOAD_FIRST>
-__global__ __launch_bounds__(LOAD_FIRST ? kWave : kMaxRowBlock) void permute_fp8_kernel(
-    RowArgs a, int nchunks, int64_t item0) {
-  const int lane = lane_id();
-  const int wv = int(threadIdx.x) >> 6;          // wave of the workgroup
-  const int nw = int(blockDim.x) >> 6;
+__global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchunks,
+                                                            int64_t item0) {
+  const int lane = threadIdx.x;
   const int H8 = a.H >> 3;
   const int H16 = a.H >> 4;
   // scale words per row: one per group, or one per four groups (UE8M0)
@@ -178,7 +150,7 @@ __global__ __launch_bounds__(LOAD_FIRST ? kWave : kMaxRowBlock) void permute_fp8
   u32x4* dq = static_cast<u32x4*>(a.out);
   const int64_t item = item0 + blockIdx.x;
   const int64_t t = udiv(item, nchunks);
-  const int p0 = (int(item - t * nchunks) * nw + wv) * (kWave * IT);
+  const int p0 = int(item - t * nchunks) * (kWave * IT);
   // LOAD_FIRST: the row is loaded before its destinations are known (as in
   // the bf16 permute), so both round trips overlap; the sparse
   // expert-batched fill looks the rows up first and skips tokens with none.
@@ -539,40 +511,24 @@ void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
   // one moved the rows fastest: short-lived waves keep the stores streaming,
   // while larger chunks at full occupancy put so many rows in flight that
   // the stores slow down.
-  if (a.sparse) {
-    const int64_t H8 = a.H >> 3;
-    const int64_t nch = (H8 + kMaxRowBlock - 1) / kMaxRowBlock;
-    const int threads = int(((H8 + nch - 1) / nch + kWave - 1) / kWave) * kWave;
-    for_each_launch(a.T * nch, [&](int64_t i0, unsigned g) {
-      batched_fill_bf16_kernel<KMAX><<<g, threads, 0, s>>>(a, int(nch), i0);
-    });
-    return;
-  }
   const int nchunks = int(((a.H >> 3) + kPermuteBlock - 1) / kPermuteBlock);
   for_each_launch(a.T * nchunks, [&](int64_t i0, unsigned g) {
-    permute_bf16_kernel<KMAX, 1, true><<<g, kPermuteBlock, a.capped ? kPermuteLdsCap : 0u, s>>>(
-        a, nchunks, i0);
+    if (a.sparse)
+      permute_bf16_kernel<KMAX, 1, false><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
+    else
+      permute_bf16_kernel<KMAX, 1, true><<<g, kPermuteBlock, a.capped ? kPermuteLdsCap : 0u, s>>>(
+          a, nchunks, i0);
   });
 }
 
 template <int KMAX, int IT, int SFMT>
 void launch_permute_fp8_p(const RowArgs& a, Split sp, hipStream_t s) {
-  if (a.sparse) {
-    // sp.nchunks one-wave chunks per row, grouped into workgroups of up to
-    // kMaxRowBlock / kWave waves
-    const int most = kMaxRowBlock / kWave;
-    const int nch = (sp.nchunks + most - 1) / most;
-    const int waves = (sp.nchunks + nch - 1) / nch;
-    // every workgroup holds `waves` whole chunks: the grid covers
-    // nch * waves >= sp.nchunks chunks, the excess lanes fail p < H16
-    for_each_launch(a.T * nch, [&](int64_t i0, unsigned g) {
-      permute_fp8_kernel<KMAX, IT, SFMT, false><<<g, waves * kWave, 0, s>>>(a, nch, i0);
-    });
-    return;
-  }
   for_each_launch(a.T * sp.nchunks, [&](int64_t i0, unsigned g) {
-    permute_fp8_kernel<KMAX, IT, SFMT, true><<<g, kWave, a.capped ? kFp8PermuteLdsCap : 0u, s>>>(
-        a, sp.nchunks, i0);
+    if (a.sparse)
+      permute_fp8_kernel<KMAX, IT, SFMT, false><<<g, kWave, 0, s>>>(a, sp.nchunks, i0);
+    else
+      permute_fp8_kernel<KMAX, IT, SFMT, true><<<g, kWave, a.capped ? kFp8PermuteLdsCap : 0u, s>>>(
+          a, sp.nchunks, i0);
   });
 }
 
