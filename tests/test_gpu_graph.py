@@ -1,0 +1,110 @@
+"""The library's calls under HIP graph capture: the send path (counts and
+layout in one launch, permute, combine), the batched fp8 layout and the
+regroup by expert are captured once and replayed several times, with eager
+work and synchronizations between the replays; every replay must equal the
+eager result bit for bit.  The calls enqueue kernels only (no memset, no
+allocation, no host sync), and their workspaces rearm themselves, so a
+replayed barrier or lookback sees a fresh generation each time."""
+
+import numpy as np
+import pytest
+import torch
+
+from epgen import make_hidden, make_routing, spec
+from tests.gpu_helpers import to_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+import combine_ep_send_amd as ep  # noqa: E402
+
+
+def _replays(capture_fn, outputs, n=4):
+    """Capture capture_fn, then replay it n times; return host copies of the
+    outputs after each replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        capture_fn()                       # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        capture_fn()
+    torch.cuda.synchronize()
+    got = []
+    for i in range(n):
+        for o in outputs:                  # eager work between replays
+            o.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got.append([o.view(torch.uint8).cpu().numpy().copy() for o in outputs])
+    return got
+
+
+def test_send_path_graph_replays():
+    s = spec("skewed_t16384", T=3000, H=1024)
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    T, K, P, El, H = s.T, s.K, s.P, s.E_local, s.H
+    cap = T * min(K, P)
+    d_idx, d_w, d_x = to_dev(idx), to_dev(w), to_dev(x)
+    counts, lay = ep.ep_dispatch_layout(d_idx, d_w, P, El, cap)
+    send_x = ep.ep_dispatch_permute(d_x, lay.token_row, cap)
+    out = ep.ep_combine(send_x, lay.token_row, d_w)
+    torch.cuda.synchronize()
+    N = int(counts.send_counts.sum().item())
+    eager = [lay.token_row.clone(), lay.send_token_idx[:N].clone(), send_x[:N].clone(), out.clone()]
+    ws = ep.workspace_for(ep.ep_dispatch_layout_workspace_bytes(T, P, El), d_x.device,
+                          kind="graph")
+
+    def step():
+        ep.ep_dispatch_layout(d_idx, d_w, P, El, cap, counts=counts, out=lay, workspace=ws)
+        ep.ep_dispatch_permute(d_x, lay.token_row, cap, out=send_x)
+        ep.ep_combine(send_x, lay.token_row, d_w, out=out)
+
+    outs = [lay.token_row, lay.send_token_idx[:N], send_x[:N], out]
+    for rep in _replays(step, outs):
+        for got, want in zip(rep, eager):
+            assert np.array_equal(got, want.view(torch.uint8).cpu().numpy())
+    hdr = ws[:16].view(torch.int32).cpu().numpy()
+    assert hdr[0] == 0 and hdr[3] == 0          # barrier arrivals rearmed, no time-out
+
+
+def test_batched_fp8_and_regroup_graph_replays():
+    s = spec("batched_t8192", T=2000, H=1536)
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    T, K, El, H = s.T, s.K, s.E_local, s.H
+    d_idx, d_x, d_w = to_dev(idx), to_dev(x), to_dev(w)
+    M = 256
+    bq, bs, tpe, trow = ep.ep_batched_prepare_fp8(d_x, d_idx, 0, El, M, scale_fmt="ue8m0",
+                                                  scale_col_major=True)
+    # regroup of this GPU's send buffer (P = 8 destinations) by local expert
+    P = s.P
+    counts, lay = ep.ep_dispatch_layout(d_idx, d_w, P, El, T * min(K, P))
+    N = int(counts.send_counts.sum().item())
+    send_x = ep.ep_dispatch_permute(d_x, lay.token_row, T * min(K, P))
+    reg = ep.ep_regroup_by_expert(send_x[:N], lay.send_idx[:N], lay.send_w[:N], El, 16,
+                                  row_group=lay.send_rank[:N], num_groups=P)
+    torch.cuda.synchronize()
+    M_r = int(reg.expert_offsets[-1].item())
+    bs_mem = bs.transpose(1, 2)           # the scales in memory order (contiguous)
+    eager = [bq.clone(), bs_mem.clone(), tpe.clone(), trow.clone(),
+             reg.perm_x[:M_r].clone(), reg.row_map.clone(), reg.expert_offsets.clone()]
+    ws_b = ep.workspace_for(ep.ep_batched_workspace_bytes(T, El, M), d_x.device, kind="graph_b")
+    ws_r = ep.workspace_for(ep.ep_regroup_workspace_bytes(N, P * El), d_x.device, kind="graph_r")
+
+    def step():
+        ep.ep_batched_prepare_fp8(d_x, d_idx, 0, El, M, scale_fmt="ue8m0", scale_col_major=True,
+                                  out=bq, out_scale=bs, tokens_per_expert=tpe, token_row=trow,
+                                  workspace=ws_b)
+        ep.ep_regroup_by_expert(send_x[:N], lay.send_idx[:N], lay.send_w[:N], El, 16,
+                                row_group=lay.send_rank[:N], num_groups=P, out=reg,
+                                workspace=ws_r)
+
+    outs = [bq, bs_mem, tpe, trow, reg.perm_x[:M_r], reg.row_map, reg.expert_offsets]
+    for rep in _replays(step, outs):
+        for got, want in zip(rep, eager):
+            assert np.array_equal(got, want.view(torch.uint8).cpu().numpy())
