@@ -35,6 +35,8 @@ def _rand_bf16(rng, shape):
     (1000, 7168, 256, 8, 32, "uniform", 0.0),
     (300, 64, 16, 16, 4, "uniform", 0.1),
     (700, 256, 30, 5, 6, "uniform", 0.0),
+    (300, 16384, 16, 4, 8, "uniform", 0.0),    # few rows per token (the sparse form), 3 chunks
+    (400, 9216, 64, 8, 8, "zipf", 0.05),       # many rows per token, 2 ragged chunks
 ])
 def test_partial_sums_and_biases(T, H, E, K, P, routing, unrouted):
     print(f"case: T={T} H={H} E={E} K={K} P={P}", flush=True)

@@ -139,6 +139,8 @@ def test_hand_worked_example(golden):
     (300, 64, 16, 16, 4, "uniform", 0.1),         # K = 16
     (513, 8, 4, 1, 4, "uniform", 0.0),            # K = 1, H = 8
     (400, 128, 96, 3, 1, "uniform", 0.0),         # one destination
+    (300, 16384, 64, 4, 8, "uniform", 0.0),       # H beyond one workgroup's row (2 combine chunks)
+    (200, 9216, 64, 6, 8, "zipf", 0.05),          # ragged combine chunks (2 x 576 pieces)
 ])
 def test_send_path_matches_oracle(T, H, E, K, P, routing, unrouted):
     _print_case(T=T, H=H, E=E, K=K, P=P, routing=routing)
@@ -153,7 +155,8 @@ def test_send_path_other_seeds(seed):
     check_send_path(idx, w, x, 8, 8)
 
 
-@pytest.mark.parametrize("T,H,K,P", [(600, 1024, 8, 32), (257, 128, 4, 8), (64, 7168, 8, 32)])
+@pytest.mark.parametrize("T,H,K,P", [(600, 1024, 8, 32), (257, 128, 4, 8), (64, 7168, 8, 32),
+                                     (100, 16384, 8, 32)])
 def test_fp8_path_matches_oracle(T, H, K, P):
     _print_case(T=T, H=H, K=K, P=P, fp8=True)
     s, idx, w, x = send_case(T, H, 256, K, P)
