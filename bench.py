@@ -711,9 +711,10 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_tokens or {"skewed_t16384": 16384, "uniform_t4096": 4096, "tiny": 256,
-                                "batched_t8192": 8192, "fp8_t32768": 6144,
-                                "batched_fp8_t8192": 8192, "expert_major_t16384": 16384}.get(s.name, 1024)
+        whole = {"skewed_t16384": 16384, "uniform_t4096": 4096, "tiny": 256,
+                 "batched_t8192": 8192, "fp8_t32768": 6144, "batched_fp8_t8192": 8192,
+                 "expert_major_t16384": 16384}
+        n = args.cpu_tokens or whole.get(s.name, 1024)
         log(f"[bench] timing the CPU oracle on {n} tokens")
         result["cpu_baseline"] = cpu_baseline(s, n)
     print(json.dumps(result), flush=True)
