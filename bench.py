@@ -500,8 +500,9 @@ def cpu_baseline(s, budget_tokens):
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": f"first {T} tokens of the {s.name} workload (same generator and seed), "
-                  f"all phases, numpy single-threaded" +
+        "sample": (f"the whole {s.name} workload" if T == s.T else
+                   f"first {T} tokens of the {s.name} workload") +
+                  " (same generator and seed), all phases, numpy single-threaded" +
                   (f", max_num_tokens scaled to {-(-s.max_num_tokens * T // s.T)}"
                    if s.layout == "batched" and s.fp8 else ""),
     }
