@@ -48,6 +48,12 @@
  *    be NULL.
  *  - Limits: 1 <= K <= 16; T < 2^30; P and E_local <= 1024; E <= 8192;
  *    H a positive multiple of 8 (of 128 for fp8); every row index fits int32.
+ *  - Workspaces: each serves one family of calls, whose control words it
+ *    keeps: ep_compute_send_counts; the scans (ep_build_send_layout,
+ *    ep_batched_prepare, ep_batched_prepare_fp8); or the one-launch layouts
+ *    (ep_dispatch_layout, ep_regroup_by_expert).  Zero it once, size it for
+ *    the largest call, and do not hand it to a call of another family or to
+ *    two calls that may run at the same time.
  */
 #ifndef EPDC_H
 #define EPDC_H
