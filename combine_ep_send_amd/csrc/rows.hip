@@ -466,7 +466,9 @@ __global__ __launch_bounds__(kSparseBlock) void combine_sparse_kernel(CombineArg
 
 // ---- launch shapes -----------------------------------------------------------
 
-constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+// A launch may span at most 2^32-1 work-items per grid dimension, so the
+// largest grid in workgroups depends on the workgroup size.
+constexpr int64_t max_blocks(int threads) { return int64_t(UINT32_MAX) / threads; }
 
 // Occupancy caps of the dense (token-major) permutes.  An unused dynamic LDS
 // allocation limits how many workgroups share a compute unit (160 KiB of LDS
@@ -483,12 +485,13 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 constexpr unsigned kPermuteLdsCap = 18 * 1024;
 constexpr unsigned kFp8PermuteLdsCap = 10 * 1024;
 
-// One workgroup per item; grids beyond the 2^31-1 limit go out as several
-// launches, each told its first item.
+// One workgroup of `threads` per item; grids beyond the work-item limit go
+// out as several launches, each told its first item.
 template <typename Launch>
-void for_each_launch(int64_t items, Launch launch) {
-  for (int64_t i0 = 0; i0 < items; i0 += kMaxGrid)
-    launch(i0, unsigned(items - i0 < kMaxGrid ? items - i0 : kMaxGrid));
+void for_each_launch(int64_t items, int threads, Launch launch) {
+  const int64_t most = max_blocks(threads);
+  for (int64_t i0 = 0; i0 < items; i0 += most)
+    launch(i0, unsigned(items - i0 < most ? items - i0 : most));
 }
 
 // Split a row of `pieces` per-lane-sized units into the fewest chunks of at
@@ -512,7 +515,7 @@ void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
   // while larger chunks at full occupancy put so many rows in flight that
   // the stores slow down.
   const int nchunks = int(((a.H >> 3) + kPermuteBlock - 1) / kPermuteBlock);
-  for_each_launch(a.T * nchunks, [&](int64_t i0, unsigned g) {
+  for_each_launch(a.T * nchunks, kPermuteBlock, [&](int64_t i0, unsigned g) {
     if (a.sparse)
       permute_bf16_kernel<KMAX, 1, false><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
     else
@@ -523,7 +526,7 @@ void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
 
 template <int KMAX, int IT, int SFMT>
 void launch_permute_fp8_p(const RowArgs& a, Split sp, hipStream_t s) {
-  for_each_launch(a.T * sp.nchunks, [&](int64_t i0, unsigned g) {
+  for_each_launch(a.T * sp.nchunks, kWave, [&](int64_t i0, unsigned g) {
     if (a.sparse)
       permute_fp8_kernel<KMAX, IT, SFMT, false><<<g, kWave, 0, s>>>(a, sp.nchunks, i0);
     else
@@ -555,7 +558,7 @@ void launch_combine_k(const CombineArgs& a, hipStream_t s) {
     const int per = int((H8 + kSparseBlock - 1) / kSparseBlock) < 7
                         ? int((H8 + kSparseBlock - 1) / kSparseBlock) : 7;
     const int64_t nch = (H8 + int64_t(kSparseBlock) * per - 1) / (int64_t(kSparseBlock) * per);
-    for_each_launch(a.T * nch, [&](int64_t i0, unsigned g) {
+    for_each_launch(a.T * nch, kSparseBlock, [&](int64_t i0, unsigned g) {
 #define EPDC_SPARSE(P)                                                                    \
   if (a.w)                                                                                \
     combine_sparse_kernel<KMAX, true, P><<<g, kSparseBlock, 0, s>>>(a, int(nch), i0);    \
@@ -579,7 +582,7 @@ void launch_combine_k(const CombineArgs& a, hipStream_t s) {
   const int64_t nch = (H8 + kMaxRowBlock - 1) / kMaxRowBlock;
   const int64_t per_chunk = (H8 + nch - 1) / nch;
   const int threads = int((per_chunk + kWave - 1) / kWave) * kWave;
-  for_each_launch(a.T * nch, [&](int64_t i0, unsigned g) {
+  for_each_launch(a.T * nch, threads, [&](int64_t i0, unsigned g) {
     if (a.w)
       combine_kernel<KMAX, true><<<g, threads, 0, s>>>(a, int(nch), i0);
     else
@@ -623,7 +626,8 @@ hipError_t launch_zero_pad(const PadArgs& a, hipStream_t s) {
   const int64_t region = a.max_tokens * a.row_pieces;
   if (region == 0 || a.E_local == 0) return hipSuccess;
   const int64_t gx = (region + kBlock - 1) / kBlock;
-  const dim3 grid{unsigned(gx < kMaxGrid ? gx : kMaxGrid), unsigned(a.E_local), 1u};
+  const dim3 grid{unsigned(gx < max_blocks(kBlock) ? gx : max_blocks(kBlock)), unsigned(a.E_local),
+                  1u};
   zero_pad_kernel<<<grid, kBlock, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -632,7 +636,7 @@ hipError_t launch_scale_pad(const ScalePadArgs& a, hipStream_t s) {
   const int64_t longest = a.col_major ? a.max_tokens : a.max_tokens * a.units;
   if (longest == 0 || a.E_local == 0) return hipSuccess;
   const int64_t gx = (longest + kBlock - 1) / kBlock;
-  if (gx > kMaxGrid) return hipErrorInvalidValue;
+  if (gx > max_blocks(kBlock)) return hipErrorInvalidValue;
   const dim3 grid{unsigned(gx), unsigned(a.E_local), 1u};
   scale_pad_kernel<<<grid, kBlock, 0, s>>>(a);
   return hipGetLastError();
