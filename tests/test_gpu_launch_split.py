@@ -4,10 +4,12 @@ several launches, each told its first item.  Narrow rows make such token
 counts cheap: 34 million tokens of 8 channels need 34 million 128-thread
 workgroups in the bf16 permute and the sparse combine (two launches each),
 68 million need more than one launch of the 64-thread fp8 permute and dense
-combine.  The full outputs are checked by properties that hold at any size
+combine, and the expert-batched fills run just under and just past the
+limit.  The full outputs are checked by properties that hold at any size
 (with one slot per token the permute is a scatter by a permutation and the
-unweighted combine its gather), and sampled tokens on both sides of each
-split point against the CPU oracle."""
+unweighted combine its gather; the batched routing has closed-form counts
+and slots), and sampled tokens on both sides of each split point against
+the CPU oracle."""
 
 import numpy as np
 import pytest
@@ -29,10 +31,14 @@ def _bits(t):
 
 
 def _samples(T, split, n=96, seed=0):
-    """Sorted token ids: both ends, both sides of the split and random ones."""
+    """Sorted ids in [0, T): both ends, both sides of the split and random
+    ones."""
     r = np.random.default_rng(seed)
     edge = [0, 1, split - 2, split - 1, split, split + 1, T - 2, T - 1]
-    return np.unique(np.concatenate([edge, r.integers(0, T, n)])).astype(np.int64)
+    ids = np.unique(np.concatenate([edge, r.integers(0, T, n)])).astype(np.int64)
+    ids = ids[(ids >= 0) & (ids < T)]
+    assert len(ids) and ids[0] >= 0 and ids[-1] < T
+    return ids
 
 
 def _inputs(T, H, seed):
@@ -114,3 +120,67 @@ def test_dense_combine_split_launches():
     acc = w[:, :1] * yf[r0]
     acc = acc + torch.where((r1 >= 0)[:, None], w[:, 1:] * yf[r1.clamp(min=0)], 0.0)
     assert torch.equal(out, acc.to(torch.bfloat16))
+
+
+def _batched_expect(T, El, M):
+    """Routing of the batched launch cases: token t names expert t % (El+1),
+    so expert e < El takes tokens e, e+El+1, ... in order and the last id is
+    not local; counts, slot and token_row follow in closed form."""
+    t = torch.arange(T, device="cuda", dtype=torch.int64)
+    idx = (t % (El + 1)).view(T, 1)
+    cnt = [(T - e + El) // (El + 1) for e in range(El)]
+    e_of = idx[:, 0]
+    trow = torch.where(e_of < El, e_of * M + t // (El + 1), -1).to(torch.int32).view(T, 1)
+    return idx, cnt, trow
+
+
+@pytest.mark.parametrize("T", [33_500_000, 34_000_000])
+def test_batched_bf16_one_launch_and_split(T):
+    """The expert-batched fill over one-piece rows: 33.5M tokens fit one
+    launch of the sparse permute, just under the limit; 34M need two."""
+    H, El = 8, 2
+    M = T
+    print(f"case: batched bf16, T={T} H={H} E_local={El} max={M}", flush=True)
+    x, _ = _inputs(T, H, 14)
+    idx, cnt, trow = _batched_expect(T, El, M)
+    b_x = torch.empty((El, M, H), dtype=torch.bfloat16, device="cuda")
+    b_x.view(torch.int16).fill_(-1)
+    b, tpe, tr = ep.ep_batched_prepare(x, idx, 0, El, M, out=b_x)
+    assert host(tpe).tolist() == cnt
+    assert torch.equal(tr, trow)
+    for e in range(El):
+        assert torch.equal(b[e, :cnt[e]], x[e::El + 1])
+        assert int(torch.count_nonzero(b[e, cnt[e]:].view(torch.int16))) == 0
+
+
+@pytest.mark.parametrize("T", [66_000_000, 68_000_000])
+def test_batched_fp8_one_launch_and_split(T):
+    """As above for the fp8 layout (one-wave fill items): 66M tokens in one
+    launch, 68M in two; sampled rows against the oracle, every data row
+    written, every padding code and scale zero."""
+    H, El = 128, 2
+    M = T
+    print(f"case: batched fp8, T={T} H={H} E_local={El} max={M}", flush=True)
+    x, _ = _inputs(T, H, 15)
+    idx, cnt, trow = _batched_expect(T, El, M)
+    q = torch.full((El, M, H), 0xFF, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sc = ep.batched_scale_like(El, M, H, "f32", False, "cuda")
+    sc.fill_(float("nan"))
+    bq, bs, tpe, tr = ep.ep_batched_prepare_fp8(x, idx, 0, El, M, scale_fmt="f32", out=q,
+                                                out_scale=sc)
+    assert host(tpe).tolist() == cnt
+    assert torch.equal(tr, trow)
+    for e in range(El):
+        assert not bool((bq[e, :cnt[e]].view(torch.uint8) == 0xFF).any())
+        assert not bool(torch.isnan(bs[e, :cnt[e]]).any())
+        assert int(torch.count_nonzero(bq[e, cnt[e]:].view(torch.uint8))) == 0
+        assert int(torch.count_nonzero(bs[e, cnt[e]:])) == 0
+    split_tok = min(T, LIMIT // 64)       # first token of a second fp8 permute launch
+    for e in range(El):
+        slots = _samples(cnt[e], (split_tok - e) // (El + 1), n=48, seed=e)
+        assert slots[-1] < cnt[e] and slots[-1] * (El + 1) + e < T   # in bounds of x and b_q
+        toks = torch.from_numpy(slots * (El + 1) + e).cuda()
+        oq, osc = O.quantize_rows_fp8(_bits(x[toks]), "f32")
+        sl = torch.from_numpy(slots).cuda()
+        assert np.array_equal(bq[e][sl].view(torch.uint8).cpu().numpy(), oq)
+        assert np.array_equal(bs[e][sl].cpu().numpy().view(np.uint32), osc.view(np.uint32))
