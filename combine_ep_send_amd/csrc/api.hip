@@ -2,6 +2,8 @@
 // Nothing here allocates, frees or synchronizes.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/epdc.h"
 #include "epdc_launch.h"
 
@@ -48,16 +50,20 @@ void set_fused_workspace(FusedArgs& a, void* ws, int64_t bins, int64_t row_words
   a.two_pass = fused_two_pass(groups, bins, a.waves);
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; callers on
+// several host threads may race to fill an entry, all with the same value).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxFusedGroups;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
     n = 1;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
