@@ -182,12 +182,24 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
       f[2 * i] = bf16_lo(w[i]);
       f[2 * i + 1] = bf16_hi(w[i]);
     }
-    float amax = 0.0f;
+    // amax on the bits: for magnitudes (sign cleared) the unsigned order of
+    // the fp32 bit patterns is the numeric order, and a NaN (bits above
+    // 0x7F800000) is left out.  Float max instructions would return a NaN
+    // for a signalling NaN input, which the next max then drops, losing the
+    // elements before it.
+    uint32_t mbits = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    for (int i = 0; i < 8; ++i) {
+      uint32_t lo = (w[i] << 16) & 0x7FFFFFFFu;
+      uint32_t hi = w[i] & 0x7FFF0000u;
+      lo = lo > 0x7F800000u ? 0u : lo;
+      hi = hi > 0x7F800000u ? 0u : hi;
+      mbits = max(mbits, max(lo, hi));
+    }
+    mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), 1)));
+    mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), 2)));
+    mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), 4)));
+    const float amax = __uint_as_float(mbits);
     float scale = amax / 448.0f;
     if (SFMT != kScaleF32) scale = pow2_ceil(scale);
     float divisor = scale;
@@ -203,7 +215,8 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
     }
     uint32_t c[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = amax > 0.0f ? e4m3_encode(f[i] / divisor) : 0u;
+    for (int i = 0; i < 16; ++i)
+      c[i] = amax > 0.0f ? e4m3_encode(f[i] / divisor) : (f[i] != f[i] ? 0x7Fu : 0u);
     q[it] = u32x4{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
                   pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15])};
   }

@@ -318,7 +318,10 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx,
  *               channels: amax = max |x|, scale = fp32(amax / 448),
  *               code = e4m3(fp32(x / scale)) rounded to nearest, ties to
  *               even, saturating at +-448, sign kept; amax == 0 gives
- *               scale 0 and codes 0x00.  Inputs must be finite.
+ *               scale 0 and codes 0x00.  Non-finite inputs: NaN elements
+ *               do not count toward amax and give the NaN code 0x7F; a
+ *               group holding an infinity gets an infinite scale (finite
+ *               elements then give zeros, infinite ones 0x7F).
  *   send_scale  NULL for bf16.
  */
 int ep_dispatch_permute(const void* x, int64_t num_tokens, int hidden,
@@ -374,7 +377,8 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx,
  *                   [E_local, max, H/512] int32; H must be a multiple of 512.
  * code = e4m3(fp32(x / scale)) with scale the stored value (2^(byte-127) for
  * UE8M0), rounded to nearest, ties to even, saturating at +-448, sign kept;
- * amax == 0 gives codes 0x00 and scale 0 (byte 0).  Inputs must be finite.
+ * amax == 0 gives codes 0x00 and scale 0 (byte 0).  Non-finite inputs as in
+ * ep_dispatch_permute; an infinite scale is stored as such (UE8M0 byte 0xFF).
  * Every padding slot (past an expert's count) gets zero codes and zero
  * scale words, each byte written once.
  *
@@ -418,7 +422,8 @@ int ep_batched_prepare_fp8(const void* x, const int64_t* topk_idx,
  * at +0.0) in ascending k.  Without (topk_weights == NULL): each distinct row
  * of token t is added once, in the order of its first slot.  The biases that
  * are given are added after the expert terms, bias0 first; the sum is rounded
- * once to bf16, to nearest with ties to even.  Rows r >= num_rows are
+ * once to bf16, to nearest with ties to even (past the largest bf16: an
+ * infinity; any NaN: the quiet NaN 0x7FC0).  Rows r >= num_rows are
  * skipped.  Tokens with no row give +0 (plus the biases).
  *
  *   y             [num_rows, H] bf16 in   expert outputs (send rows, or the

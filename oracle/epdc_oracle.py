@@ -206,11 +206,15 @@ def bf16_to_f32(bits):
 
 
 def f32_to_bf16(values):
-    """Round float32 to bf16, to nearest with ties to even (finite inputs).
+    """Round float32 to bf16, to nearest with ties to even.
 
     bf16 keeps the upper 16 bits of binary32.  The two candidates are the
     truncated magnitude and the next bf16 magnitude up; the dropped 16 bits
-    decide, and an exact half picks the candidate whose last kept bit is 0.
+    decide, and an exact half picks the candidate whose last kept bit is 0
+    (past the largest bf16 the next magnitude up is infinity).  The pages
+    leave NaN open; reading: any NaN gives the canonical quiet NaN 0x7FC0,
+    since the sign and payload of a NaN produced by arithmetic differ from
+    one machine to another.
     """
     u = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32)
     lower = u & np.uint32(0xFFFF0000)
@@ -220,7 +224,9 @@ def f32_to_bf16(values):
     lower_even = ((lower >> np.uint32(16)) & np.uint32(1)) == 0
     pick_upper = (rem > half) | ((rem == half) & ~lower_even)
     out = np.where(pick_upper, upper, lower)
-    return (out >> np.uint32(16)).astype(np.uint16)
+    out = (out >> np.uint32(16)).astype(np.uint16)
+    is_nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    return np.where(is_nan, np.uint16(0x7FC0), out).astype(np.uint16)
 
 
 def e4m3_decode(codes):
@@ -242,11 +248,13 @@ _E4M3_POS = e4m3_decode(np.arange(0x7F))
 
 def e4m3_encode(values):
     """Nearest OCP E4M3 code of each float32 value, ties to the even code
-    (mantissa LSB 0); magnitudes at or above 448 saturate to 448; the sign
-    bit is kept, so -0.0 and negative values that round to zero give 0x80."""
+    (mantissa LSB 0); magnitudes at or above 448, infinities included,
+    saturate to 448; the sign bit is kept, so -0.0 and negative values that
+    round to zero give 0x80.  Any NaN gives the NaN code 0x7F."""
     v = np.asarray(values, dtype=np.float32)
     sign = (v.view(np.uint32) >> np.uint32(31)).astype(np.int64)
-    mag = np.abs(v.astype(np.float64))
+    with np.errstate(invalid="ignore"):        # a signalling NaN quietens
+        mag = np.abs(v.astype(np.float64))
     hi = np.searchsorted(_E4M3_POS, mag, side="left")        # POS[hi] >= mag
     hi = np.clip(hi, 0, len(_E4M3_POS) - 1)
     lo = np.clip(hi - 1, 0, len(_E4M3_POS) - 1)
@@ -256,17 +264,21 @@ def e4m3_encode(values):
     code = np.where(take_hi, hi, lo)
     code = np.where(mag >= FP8_MAX, 0x7E, code)
     code = np.where(mag == 0.0, 0, code)
-    return (code | (sign << 7)).astype(np.uint8)
+    code = code | (sign << 7)
+    return np.where(np.isnan(mag), 0x7F, code).astype(np.uint8)
 
 
 def round_scale_pow2(s):
     """[uccl] Buffer.low_latency_dispatch ``round_scale``: the scale becomes a
     power of two.  Reading: the smallest power of two that is >= s, so that
-    x / scale still lies within the e4m3 range; 0 stays 0.  Input and output
+    x / scale still lies within the e4m3 range; 0 stays 0, and an infinite
+    scale (a group holding an infinity) stays infinite.  Input and output
     float32 (every such power of two from 2^-149 up is a float32)."""
     s64 = np.asarray(s, dtype=np.float32).astype(np.float64)
-    m, e = np.frexp(s64)                    # s = m * 2^e with 0.5 <= m < 1
+    fin = np.isfinite(s64)
+    m, e = np.frexp(np.where(fin, s64, 1.0))     # s = m * 2^e with 0.5 <= m < 1
     p = np.where(m == 0.5, s64, np.ldexp(1.0, e))
+    p = np.where(fin, p, s64)
     return np.where(s64 == 0.0, 0.0, p).astype(np.float32)
 
 
@@ -276,17 +288,22 @@ def ue8m0_encode(p):
     so 2^e is stored as e + 127.  Powers below 2^-127, and 0, take the
     smallest code 0x00 (2^-127): a larger scale than asked for, which keeps
     x / scale in range.  The largest scale a finite bf16 group can ask for
-    is 2^120 (code 247), so no group reaches the top codes."""
+    is 2^120 (code 247), so no finite group reaches the top codes; an
+    infinite scale takes 0xFF, the code past every power (its value taken
+    as infinity, so the group's finite elements quantize to zero)."""
     p64 = np.asarray(p, dtype=np.float32).astype(np.float64)
-    e = np.frexp(p64)[1] - 1                # p = 2^e
+    e = np.frexp(np.where(np.isfinite(p64), p64, 1.0))[1] - 1      # p = 2^e
     b = np.where(p64 > 0, np.clip(e + UE8M0_BIAS, 0, 254), 0)
+    b = np.where(np.isinf(p64), 255, b)
     return b.astype(np.uint8)
 
 
 def ue8m0_decode(b):
-    """float32 value 2^(b - 127) of UE8M0 bytes 0..254."""
+    """float32 value 2^(b - 127) of UE8M0 bytes 0..254; 255 (2^128) is past
+    float32 and decodes to infinity."""
     b = np.asarray(b, dtype=np.int64)
-    return np.ldexp(1.0, b - UE8M0_BIAS).astype(np.float32)
+    with np.errstate(over="ignore"):
+        return np.ldexp(1.0, b - UE8M0_BIAS).astype(np.float32)
 
 
 def pack_ue8m0(b):
@@ -318,7 +335,11 @@ def quantize_rows_fp8(x_bits, scale_fmt="f32"):
     >= s (``pow2``, [uccl] ``round_scale``), or that power as a UE8M0 byte
     (``ue8m0``, [uccl] ``use_ue8m0``; the quantizer then divides by the
     byte's value 2^(b-127)).  q = e4m3(fl32(x / scale)).  A group whose amax
-    is 0 gets all codes 0x00 and scale 0.0 (byte 0x00 in ``ue8m0``).
+    is 0 gets all codes 0x00 and scale 0.0 (byte 0x00 in ``ue8m0``).  The
+    pages leave non-finite inputs open; reading: NaN elements do not count
+    toward amax (as a running fmax) and always encode to the NaN code 0x7F
+    (also in a group with no other non-zero element), and a group holding
+    an infinity gets an infinite scale, so its finite elements give zeros.
     Returns (uint8 [R,H], scales): float32 [R, H/128] for ``f32`` and
     ``pow2``, int32 [R, H/512] (pack_ue8m0) for ``ue8m0``.
     """
@@ -329,7 +350,7 @@ def quantize_rows_fp8(x_bits, scale_fmt="f32"):
     if H % FP8_GROUP:
         raise ValueError("H must be a multiple of 128 for fp8")
     g = x.reshape(R, H // FP8_GROUP, FP8_GROUP)
-    amax = np.abs(g).max(axis=2)
+    amax = np.where(np.isnan(g), np.float32(0.0), np.abs(g)).max(axis=2)
     scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
     if scale_fmt == "pow2":
         scale = round_scale_pow2(scale)
@@ -337,9 +358,11 @@ def quantize_rows_fp8(x_bits, scale_fmt="f32"):
         byte = ue8m0_encode(round_scale_pow2(scale))
         scale = np.where(amax > 0, ue8m0_decode(byte), np.float32(0.0)).astype(np.float32)
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    quot = (g / safe[:, :, None]).astype(np.float32)
+    with np.errstate(invalid="ignore"):           # inf / inf: NaN, encoded as such
+        quot = (g / safe[:, :, None]).astype(np.float32)
     q = e4m3_encode(quot)
-    q = np.where((scale > 0)[:, :, None], q, np.uint8(0))
+    zero_group = np.where(np.isnan(g), np.uint8(0x7F), np.uint8(0))
+    q = np.where((scale > 0)[:, :, None], q, zero_group)
     q = q.reshape(R, H).astype(np.uint8)
     if scale_fmt == "ue8m0":
         return q, pack_ue8m0(byte)

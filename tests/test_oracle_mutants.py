@@ -13,6 +13,7 @@ import types
 import numpy as np
 import pytest
 
+import tests.test_oracle_nonfinite as NF
 import tests.test_oracle_numerics as NUM
 import tests.test_oracle_routing as RT
 import tests.test_oracle_scales as SC
@@ -83,6 +84,13 @@ SCALE_PINS = [
     pin(SC, "test_pow2_and_ue8m0_codes_against_torch"),
     pin(SC, "test_batched_fp8_is_the_gather_of_quantized_rows"),
 ]
+NONFINITE_PINS = [
+    pin(NF, "test_bf16_nan_is_the_canonical_quiet_nan"),
+    pin(NF, "test_e4m3_nan_code_and_saturation"),
+    pin(NF, "test_nan_elements_do_not_move_amax"),
+    pin(NF, "test_all_nan_group_keeps_its_nans"),
+    pin(NF, "test_infinite_group_gets_an_infinite_scale"),
+]
 BATCHED_PINS = [
     pin(RT, "test_batched_equals_stable_argsort", 0, 32),
     pin(RT, "test_hand_worked_permute_and_batched", GOLDEN),
@@ -141,8 +149,26 @@ MUTANTS = {
         "scale = (amax / np.float32(240.0)).astype(np.float32)", FORMAT_PINS),
     "fp8_group_64": ("FP8_GROUP = 128", "FP8_GROUP = 64", FORMAT_PINS),
     "fp8_zero_group_sign": (
-        "q = np.where((scale > 0)[:, :, None], q, np.uint8(0))",
-        "q = np.where((scale > 0)[:, :, None], q, np.uint8(0x80))", FORMAT_PINS),
+        "zero_group = np.where(np.isnan(g), np.uint8(0x7F), np.uint8(0))",
+        "zero_group = np.where(np.isnan(g), np.uint8(0x7F), np.uint8(0x80))", FORMAT_PINS),
+    "bf16_nan_rounded_like_finite": (
+        "return np.where(is_nan, np.uint16(0x7FC0), out).astype(np.uint16)",
+        "return out.astype(np.uint16)", NONFINITE_PINS),
+    "e4m3_nan_saturates": (
+        "return np.where(np.isnan(mag), 0x7F, code).astype(np.uint8)",
+        "return np.where(np.isnan(mag), 0x7E, code).astype(np.uint8)", NONFINITE_PINS),
+    "fp8_amax_propagates_nan": (
+        "amax = np.where(np.isnan(g), np.float32(0.0), np.abs(g)).max(axis=2)",
+        "amax = np.abs(g).max(axis=2)", NONFINITE_PINS),
+    "fp8_zero_group_drops_nan": (
+        "zero_group = np.where(np.isnan(g), np.uint8(0x7F), np.uint8(0))",
+        "zero_group = np.uint8(0)", NONFINITE_PINS),
+    "ue8m0_infinite_scale_clamped": (
+        "b = np.where(np.isinf(p64), 255, b)",
+        "b = np.where(np.isinf(p64), 254, b)", NONFINITE_PINS),
+    "pow2_infinite_scale_finite": (
+        "p = np.where(fin, p, s64)",
+        "p = np.where(fin, p, 1.0)", NONFINITE_PINS),
     "regroup_no_padding": (
         "    padded = [-(-int(c) // A) * A for c in counts]",
         "    padded = [int(c) for c in counts]", REGROUP_PINS),
