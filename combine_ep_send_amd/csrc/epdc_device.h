@@ -96,30 +96,29 @@ __device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Round fp32 to bf16, to nearest with ties to even: add just under half an
-// ulp of bf16, plus one if the kept LSB is odd, then truncate (a value past
-// the largest bf16 carries into infinity).  Any NaN becomes the canonical
-// quiet NaN 0x7FC0: the carry would turn some payloads into an infinity or
-// a zero, and a NaN's sign and payload after arithmetic are not portable.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 values rounded to bf16 and packed, the first in the low half, by
+// the hardware conversion (v_cvt_pk_bf16_f32): to nearest with ties to even
+// (subnormals kept, a value past the largest bf16 becomes an infinity), and
+// a NaN stays a quiet NaN (its sign and leading payload bits).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // ---- OCP e4m3 (float8_e4m3fn) encode ----------------------------------------
 // Nearest code with ties to even, saturating at 448 (0x7E; infinities too),
-// sign kept.  Any NaN gives the NaN code 0x7F.
+// sign kept.  e4m3_encode_finite takes a non-NaN value; e4m3_encode also
+// maps any NaN to the NaN code 0x7F.
 // Normal range (|v| >= 2^-6): round the binary32 mantissa from 23 to 3 bits
 // on the raw bits (a carry moves into the exponent) and rebias 127 -> 7.
 // Below 2^-6 the codes are the uniform grid m * 2^-9, m = 0..8, so the code
 // is rint(|v| * 2^9) (the scaling is exact; rint rounds ties to even).
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+__device__ __forceinline__ uint32_t e4m3_encode_finite(float v) {
   uint32_t u = __float_as_uint(v);
   uint32_t sign = (u >> 24) & 0x80u;
   uint32_t a = u & 0x7FFFFFFFu;
   uint32_t code;
-  if (a > 0x7F800000u) return 0x7Fu;         // NaN
   if (a >= 0x43E00000u) {                    // |v| >= 448
     code = 0x7Eu;
   } else if (a < 0x3C800000u) {              // |v| < 2^-6
@@ -129,6 +128,9 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
     code = r - (120u << 3);                  // exponent bias 127 -> 7
   }
   return code | sign;
+}
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  return (__float_as_uint(v) & 0x7FFFFFFFu) > 0x7F800000u ? 0x7Fu : e4m3_encode_finite(v);
 }
 
 // ---- packed scan status words ------------------------------------------------

@@ -120,6 +120,8 @@ __global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, 
 // scale_block_rows = M > 0, at (r/M)*M*units + u*M + r%M: each block of M
 // rows (an expert's slots) stores its scales column-major.
 // ---------------------------------------------------------------------------
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return a | (b << 8) | (c << 16) | (d << 24);
 }
@@ -183,19 +185,27 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
       f[2 * i + 1] = bf16_hi(w[i]);
     }
     // amax on the bits: for magnitudes (sign cleared) the unsigned order of
-    // the fp32 bit patterns is the numeric order, and a NaN (bits above
-    // 0x7F800000) is left out.  Float max instructions would return a NaN
-    // for a signalling NaN input, which the next max then drops, losing the
-    // elements before it.
-    uint32_t mbits = 0u;
+    // the bf16 bit patterns is the numeric order, and a NaN (above 0x7F80)
+    // is left out.  Float max instructions would return a NaN for a
+    // signalling NaN input, which the next max then drops, losing the
+    // elements before it.  Both halves of each word are maxed at once; only
+    // a lane whose maximum is a NaN pattern looks again without its NaNs.
+    u16x2 m2 = {0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t lo = (w[i] << 16) & 0x7FFFFFFFu;
-      uint32_t hi = w[i] & 0x7FFF0000u;
-      lo = lo > 0x7F800000u ? 0u : lo;
-      hi = hi > 0x7F800000u ? 0u : hi;
-      mbits = max(mbits, max(lo, hi));
+    for (int i = 0; i < 8; ++i)
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    uint32_t mh = max(uint32_t(m2.x), uint32_t(m2.y));
+    const bool lane_nan = mh > 0x7F80u;
+    if (lane_nan) {
+      mh = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+        if (lo <= 0x7F80u) mh = max(mh, lo);
+        if (hi <= 0x7F80u) mh = max(mh, hi);
+      }
     }
+    uint32_t mbits = mh << 16;               // the fp32 bit pattern
     mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), 1)));
     mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), 2)));
     mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), 4)));
@@ -213,10 +223,17 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
     } else {
       sw[it] = __float_as_uint(scale);
     }
+    // A quotient can be NaN only where this lane holds a NaN or the group
+    // an infinity (infinity / infinity); such lanes take the NaN-aware form.
     uint32_t c[16];
+    if (!lane_nan && mbits != 0x7F800000u) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      c[i] = amax > 0.0f ? e4m3_encode(f[i] / divisor) : (f[i] != f[i] ? 0x7Fu : 0u);
+      for (int i = 0; i < 16; ++i) c[i] = amax > 0.0f ? e4m3_encode_finite(f[i] / divisor) : 0u;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        c[i] = amax > 0.0f ? e4m3_encode(f[i] / divisor) : (f[i] != f[i] ? 0x7Fu : 0u);
+    }
     q[it] = u32x4{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
                   pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15])};
   }
@@ -394,10 +411,10 @@ __global__ __launch_bounds__(kMaxRowBlock) void combine_kernel(CombineArgs a, in
   if (a.bias0) add_row(acc, b0);
   if (a.bias1) add_row(acc, b1);
   u32x4 o;
-  o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-  o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-  o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-  o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
   st_stream(static_cast<u32x4*>(a.out) + t * H8 + j, o);
 }
 
@@ -469,10 +486,10 @@ __global__ __launch_bounds__(kSparseBlock) void combine_sparse_kernel(CombineArg
     if (a.bias0) add_row(acc[i], ld_stream(static_cast<const u32x4*>(a.bias0) + t * H8 + j));
     if (a.bias1) add_row(acc[i], ld_stream(static_cast<const u32x4*>(a.bias1) + t * H8 + j));
     u32x4 o;
-    o.x = f32_to_bf16_rne(acc[i][0]) | (f32_to_bf16_rne(acc[i][1]) << 16);
-    o.y = f32_to_bf16_rne(acc[i][2]) | (f32_to_bf16_rne(acc[i][3]) << 16);
-    o.z = f32_to_bf16_rne(acc[i][4]) | (f32_to_bf16_rne(acc[i][5]) << 16);
-    o.w = f32_to_bf16_rne(acc[i][6]) | (f32_to_bf16_rne(acc[i][7]) << 16);
+    o.x = pack_bf16x2(acc[i][0], acc[i][1]);
+    o.y = pack_bf16x2(acc[i][2], acc[i][3]);
+    o.z = pack_bf16x2(acc[i][4], acc[i][5]);
+    o.w = pack_bf16x2(acc[i][6], acc[i][7]);
     st_stream(static_cast<u32x4*>(a.out) + t * H8 + j, o);
   }
 }

@@ -423,7 +423,8 @@ int ep_batched_prepare_fp8(const void* x, const int64_t* topk_idx,
  * of token t is added once, in the order of its first slot.  The biases that
  * are given are added after the expert terms, bias0 first; the sum is rounded
  * once to bf16, to nearest with ties to even (past the largest bf16: an
- * infinity; any NaN: the quiet NaN 0x7FC0).  Rows r >= num_rows are
+ * infinity; a NaN stays a quiet NaN, sign and payload unspecified).  Rows
+ * r >= num_rows are
  * skipped.  Tokens with no row give +0 (plus the biases).
  *
  *   y             [num_rows, H] bf16 in   expert outputs (send rows, or the

