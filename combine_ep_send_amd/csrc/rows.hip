@@ -224,18 +224,44 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
       sw[it] = __float_as_uint(scale);
     }
     // A quotient can be NaN only where this lane holds a NaN or the group
-    // an infinity (infinity / infinity); such lanes take the NaN-aware form.
-    uint32_t c[16];
+    // an infinity (infinity / infinity); such lanes take the integer encoder
+    // with its NaN rule.  Elsewhere every quotient is finite and below 464
+    // in magnitude: scale >= fl32(amax / 448) is off amax/448 by at most
+    // 2^-24 relative when normal, and by less than 0.4 % when an fp32
+    // subnormal (amax >= 2^-133, the least bf16 value).  There the hardware
+    // conversion to OCP e4m3 (v_cvt_pk_fp8_f32: nearest, ties to even, sign
+    // kept, codes of two values per instruction) gives the saturating
+    // encoder's codes; it turns magnitudes from 464 up into NaN, which such
+    // quotients never reach.  A power-of-two divisor of at least 2^-127
+    // (every UE8M0 one) is applied as a multiplication by its reciprocal, a
+    // float exactly, so both round the same real quotient once; smaller
+    // powers (pow2 scales of tiny groups) have no float reciprocal.
     if (!lane_nan && mbits != 0x7F800000u) {
+      float qv[16];
+      if (SFMT != kScaleF32 && __float_as_uint(divisor) >= 0x00400000u) {
+        const float rcp = 1.0f / divisor;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = amax > 0.0f ? e4m3_encode_finite(f[i] / divisor) : 0u;
+        for (int i = 0; i < 16; ++i) qv[i] = f[i] * rcp;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qv[i] = f[i] / divisor;
+      }
+      uint32_t wq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4 * j], qv[4 * j + 1], 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4 * j + 2], qv[4 * j + 3], wd, true);
+        wq[j] = amax > 0.0f ? uint32_t(wd) : 0u;
+      }
+      q[it] = u32x4{wq[0], wq[1], wq[2], wq[3]};
     } else {
+      uint32_t c[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         c[i] = amax > 0.0f ? e4m3_encode(f[i] / divisor) : (f[i] != f[i] ? 0x7Fu : 0u);
+      q[it] = u32x4{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
+                    pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15])};
     }
-    q[it] = u32x4{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
-                  pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15])};
   }
   const int shift = SFMT == kScaleUe8m0 ? 5 : 3;      // pieces per scale word: 32 or 8
   uint32_t* sbase = static_cast<uint32_t*>(a.out_scale);
