@@ -92,7 +92,7 @@ struct FusedArgs {
   bool vec_in;                   // K % 4 == 0 and topk_idx/topk_weights 16-byte aligned
   bool vec_out;                  // K % 4 == 0 and dest/token_row 16-byte aligned
   bool vec_iir;                  // P % 16 == 0 and is_in_rank 16-byte aligned
-  uint32_t* ctrl;                // workspace header: [0] arrivals, [2] barrier generation
+  uint32_t* ctrl;                // workspace header: [0] arrivals, [2] the count at launch
   uint32_t* rows;                // [groups, P + E + 1] published totals
   uint32_t* pref;                // [groups, P] per-group exclusive prefixes (two-pass scan)
   uint32_t* tots;                // [P] bin totals (two-pass scan)

@@ -38,22 +38,26 @@ namespace {
 
 constexpr uint32_t kBarrierSpinLimit = 1u << 22;   // sleeps (~0.1 s), then give up
 
-// Grid-wide barrier number k (1, 2, ...) of this launch.  Thread 0 of every
-// workgroup adds one arrival; the arrival that completes barrier k (the
-// (k*G)-th of the launch) publishes generation gen + k, the others wait for
-// it.  The launch's last barrier also clears the arrivals for the next call.
-// A wait that outlasts the spin limit sets an error bit instead of hanging.
-__device__ __forceinline__ void grid_sync(uint32_t* ctrl, int G, uint32_t gen, uint32_t k,
+// Grid-wide barrier number k (1, 2, ...) of this launch.  The arrivals word
+// counts on across calls: `base` is its value when the launch began (the
+// previous call's last barrier leaves it in the generation word), so
+// barrier k is complete once the count reaches base + k*G.  Thread 0 of
+// every workgroup adds one arrival and, unless its own arrival completed the
+// barrier, polls the count itself: the completing atomic publishes the
+// barrier, with no separate store to wait for.  The launch's last barrier
+// hands the final count to the next call.  A wait that outlasts the spin
+// limit sets an error bit instead of hanging.
+__device__ __forceinline__ void grid_sync(uint32_t* ctrl, int G, uint32_t base, uint32_t k,
                                           bool last) {
   __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are performed
   __syncthreads();
   if (threadIdx.x == 0) {
-    if (fetch_add_relaxed(&ctrl[kCtrlTicket], 1u) == k * uint32_t(G) - 1u) {
-      if (last) st_relaxed(&ctrl[kCtrlTicket], 0u);
-      st_relaxed(&ctrl[kCtrlEpoch], gen + k);
+    const uint32_t target = base + k * uint32_t(G);
+    if (fetch_add_relaxed(&ctrl[kCtrlTicket], 1u) + 1u == target) {
+      if (last) st_relaxed(&ctrl[kCtrlEpoch], target);
     } else {
       uint32_t spins = 0;
-      while (ld_relaxed(&ctrl[kCtrlEpoch]) == gen + k - 1u) {
+      while (int32_t(ld_relaxed(&ctrl[kCtrlTicket]) - target) < 0) {
         if (++spins > kBarrierSpinLimit) {
           fetch_or(&ctrl[kCtrlError], kErrLookbackGaveUp);
           break;
@@ -227,9 +231,9 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
   const int my_tiles = tile1 > tile0 ? int(tile1 - tile0) : 0;
   const bool want_e = MODE == kFusedSend && a.tokens_per_expert != nullptr;
 
-  // The barrier generation is read now and first used at the barrier, so
-  // its round trip overlaps the decode.
-  const uint32_t gen = tid == 0 ? ld_relaxed(&a.ctrl[kCtrlEpoch]) : 0u;
+  // The arrival count this launch starts from is read now and first used at
+  // the barrier, so its round trip overlaps the decode.
+  const uint32_t base = tid == 0 ? ld_relaxed(&a.ctrl[kCtrlEpoch]) : 0u;
   if (tid == 0) s_bad = 0;
   for (int i = tid; i < nh; i += BS) s_hist[i] = 0;
   __syncthreads();
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
   for (int i = tid; i < nh; i += BS) st_relaxed(row_out + i, uint32_t(s_hist[i]));
 
   // ---- 2. grid barrier --------------------------------------------------------
-  grid_sync(a.ctrl, G, gen, 1, !a.two_pass);
+  grid_sync(a.ctrl, G, base, 1, !a.two_pass);
 
   // ---- 3. totals, bases, expert slice -----------------------------------------
   // experts [e0, e1) are this workgroup's slice of the expert totals
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
       for (int u = 0; u < 8; ++u)
         if (vx[u]) atomicAdd(&s_etot[ex[u]], int(vx[u]));
     }
-    grid_sync(a.ctrl, G, gen, 2, true);
+    grid_sync(a.ctrl, G, base, 2, true);
     for (int b = tid; b < P; b += BS) {
       s_base[b] = int(ld_relaxed(a.pref + int64_t(g) * P + b));
       s_tot[b] = int(ld_relaxed(a.tots + b));

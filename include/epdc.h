@@ -193,8 +193,9 @@ int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights,
 
 /*
  * Bytes of workspace ep_dispatch_layout needs: a 256-byte header (uint32
- * words: [0] barrier arrivals, [2] barrier generation, [3] error flags: bit 0
- * = a barrier wait gave up) followed by G rows of P + E + 1 uint32 (one per
+ * words: [0] barrier arrivals, counted on over all calls, [2] the count at
+ * the end of the last call, [3] error flags: bit 0 = a barrier wait gave
+ * up) followed by G rows of P + E + 1 uint32 (one per
  * workgroup), G rows of P uint32 (per-workgroup prefixes) and P uint32
  * (totals), G = min(ceil(T/tile), 256) with tiles of 64 tokens for T <= 4096,
  * 128 for T <= 8192, 256 above.  Zero-filled once before first use;

@@ -152,17 +152,19 @@ def test_fused_bad_ids_and_empty():
     assert c["diag"][0] == 0
 
 
-def _barriers(T, P):
-    """Grid barriers one fused call takes: two when its groups x bins table
-    is scanned bin by bin (more than 8 entries per thread of a workgroup, at
-    most 8 bins per group).  Tiles are 64 tokens up to T = 4096, 128 up to
-    8192, 256 above (one token per thread)."""
+def _arrivals(T, P):
+    """Barrier arrivals of one fused call: one per workgroup and barrier, and
+    two barriers when the groups x bins table is scanned bin by bin (more
+    than 8 entries per thread of a workgroup, at most 8 bins per group).
+    Tiles are 64 tokens up to T = 4096, 128 up to 8192, 256 above (one token
+    per thread)."""
     waves = 1 if T <= 4096 else (2 if T <= 8192 else 4)
     tiles = max(1, -(-T // (64 * waves)))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     per = -(-tiles // min(cus, 256))
     groups = -(-tiles // per)
-    return 2 if groups * P > 8 * 64 * waves and -(-P // groups) <= 8 else 1
+    barriers = 2 if groups * P > 8 * 64 * waves and -(-P // groups) <= 8 else 1
+    return barriers * groups, barriers
 
 
 def test_fused_workspace_reused_across_calls_and_sizes():
@@ -174,7 +176,7 @@ def test_fused_workspace_reused_across_calls_and_sizes():
         idx, w = _case(T, P * 2, 4 if P >= 4 else 2, P, seed=20 + i)
         check_fused(idx, w, P, 2, workspace=ws)
     hdr = ws[:16].view(torch.int32).cpu().numpy()
-    assert hdr[0] == 0 and hdr[3] == 0        # arrivals rearmed, no barrier time-out
-    want = sum(_barriers(T, P) for T, P in sizes)
-    assert want > len(sizes)                  # some calls took the two-pass scan
-    assert hdr[2] == want                     # one generation per barrier
+    assert hdr[3] == 0                        # no barrier time-out
+    assert sum(_arrivals(T, P)[1] for T, P in sizes) > len(sizes)   # some took two barriers
+    want = sum(_arrivals(T, P)[0] for T, P in sizes)
+    assert hdr[0] == want and hdr[2] == want  # every arrival counted, handed to the next call

@@ -106,7 +106,7 @@ def test_regroup_workspace_reused():
         rx, ridx, rw, El = _received(name, T, 64, p, seed=i)
         _check(rx, ridx, rw, El, align, workspace=ws)
     hdr = ws[:16].view(torch.int32).cpu().numpy()
-    assert hdr[0] == 0 and hdr[3] == 0 and hdr[2] == 3
+    assert hdr[3] == 0 and hdr[0] > 0 and hdr[0] == hdr[2]   # no time-out; count handed on
 
 
 @pytest.mark.parametrize("name,T,H,align", [("skewed_t16384", 3000, 256, 16),
