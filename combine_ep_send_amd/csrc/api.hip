@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <initializer_list>
 
 #include "../../include/epdc.h"
 #include "epdc_launch.h"
@@ -17,6 +18,18 @@ constexpr int64_t kMaxExperts = 8192;              // LDS expert histogram
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_LAUNCH; }
+
+// Words per whole-row access of rows of K 32-bit entries: 4 when K % 4 == 0
+// and every base is 16-byte aligned, 2 when K is even and every base is
+// 8-byte aligned, else 1.
+int row_words(int K, std::initializer_list<const void*> bases) {
+  bool a16 = true, a8 = true;
+  for (const void* b : bases) {
+    a16 = a16 && aligned(b, 16);
+    a8 = a8 && aligned(b, 8);
+  }
+  return (K % 4 == 0 && a16) ? 4 : ((K % 2 == 0 && a8) ? 2 : 1);
+}
 
 // A pointer is acceptable when the array it addresses is empty or the
 // pointer is non-null and aligned to `a` bytes.
@@ -258,10 +271,11 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
   a.send_idx = send_idx;
   a.send_w = send_w;
   a.token_row = token_row;
-  a.vec_rows = (num_topk % 4) == 0 && aligned(send_idx, 16) && aligned(send_w, 16);
-  a.vec_in = (num_topk % 4) == 0 && aligned(topk_idx, 16) && aligned(topk_weights, 16);
-  a.vec_out = (num_topk % 4) == 0 && aligned(dest, 16) && aligned(token_row, 16);
-  a.vec_iir = (num_ranks % 16) == 0 && aligned(is_in_rank, 16);
+  a.rows_w = row_words(num_topk, {send_idx, send_w});
+  a.in_w = aligned(topk_idx, 16) ? row_words(num_topk, {topk_weights}) : 1;
+  a.out_w = row_words(num_topk, {dest, token_row});
+  a.iir_w = num_ranks % 16 == 0 && aligned(is_in_rank, 16) ? 4
+            : num_ranks % 8 == 0 && aligned(is_in_rank, 8) ? 2 : 1;
   a.tiles = sh.tiles;
   a.tiles_per_group = int(sh.per);
   a.waves = sh.waves;
@@ -318,7 +332,7 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   a.send_counts = tokens_per_expert;
   a.send_token_idx = perm_src;
   a.token_row = row_map;
-  a.vec_out = (num_topk % 4) == 0 && aligned(row_map, 16);
+  a.out_w = row_words(num_topk, {row_map});
   a.tiles = sh.tiles;
   a.tiles_per_group = int(sh.per);
   a.waves = sh.waves;

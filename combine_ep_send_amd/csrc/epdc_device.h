@@ -7,6 +7,7 @@
 namespace epdc {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;               // 4 waves per workgroup

@@ -88,10 +88,12 @@ struct FusedArgs {
   int32_t* send_idx;
   float* send_w;
   int32_t* token_row;
-  bool vec_rows;                 // K % 4 == 0 and send_idx/send_w 16-byte aligned
-  bool vec_in;                   // K % 4 == 0 and topk_idx/topk_weights 16-byte aligned
-  bool vec_out;                  // K % 4 == 0 and dest/token_row 16-byte aligned
-  bool vec_iir;                  // P % 16 == 0 and is_in_rank 16-byte aligned
+  // Words per load or store of a whole row, where K (P for is_in_rank) and
+  // the pointers allow it: 4 (16 bytes), 2 (8 bytes) or 1.
+  int rows_w;                    // send_idx / send_w rows
+  int in_w;                      // topk_weights rows (topk_idx in 16-byte pairs when >= 2)
+  int out_w;                     // dest / token_row rows
+  int iir_w;                     // is_in_rank rows (bytes: 16, 8 or 4 per store)
   uint32_t* ctrl;                // workspace header: [0] arrivals, [2] the count at launch
   uint32_t* rows;                // [groups, P + E + 1] published totals
   uint32_t* pref;                // [groups, P] per-group exclusive prefixes (two-pass scan)

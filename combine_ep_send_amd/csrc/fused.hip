@@ -134,23 +134,33 @@ __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid
     }
     return;
   }
-  if (valid && a.vec_in && a.K == KMAX) {
-    // whole rows of ids and weights as 16-byte loads
+  if (valid && a.in_w >= 2 && a.K == KMAX) {
+    // whole rows: ids as 16-byte pairs, weights as 16- or 8-byte pieces
     const u32x4* pi = reinterpret_cast<const u32x4*>(a.topk_idx + t * KMAX);
-    const u32x4* pw = reinterpret_cast<const u32x4*>(a.topk_weights + t * KMAX);
 #pragma unroll
     for (int q = 0; q < KMAX / 2; ++q) {
       const u32x4 v = pi[q];
       s.ids[2 * q] = int64_t((uint64_t(v.y) << 32) | v.x);
       s.ids[2 * q + 1] = int64_t((uint64_t(v.w) << 32) | v.z);
     }
+    if (KMAX % 4 == 0 && a.in_w == 4) {
+      const u32x4* pw = reinterpret_cast<const u32x4*>(a.topk_weights + t * KMAX);
 #pragma unroll
-    for (int q = 0; q < KMAX / 4; ++q) {
-      const u32x4 v = pw[q];
-      s.wts[4 * q] = __uint_as_float(v.x);
-      s.wts[4 * q + 1] = __uint_as_float(v.y);
-      s.wts[4 * q + 2] = __uint_as_float(v.z);
-      s.wts[4 * q + 3] = __uint_as_float(v.w);
+      for (int q = 0; q < KMAX / 4; ++q) {
+        const u32x4 v = pw[q];
+        s.wts[4 * q] = __uint_as_float(v.x);
+        s.wts[4 * q + 1] = __uint_as_float(v.y);
+        s.wts[4 * q + 2] = __uint_as_float(v.z);
+        s.wts[4 * q + 3] = __uint_as_float(v.w);
+      }
+    } else {
+      const u32x2* pw = reinterpret_cast<const u32x2*>(a.topk_weights + t * KMAX);
+#pragma unroll
+      for (int q = 0; q < KMAX / 2; ++q) {
+        const u32x2 v = pw[q];
+        s.wts[2 * q] = __uint_as_float(v.x);
+        s.wts[2 * q + 1] = __uint_as_float(v.y);
+      }
     }
   } else {
 #pragma unroll
@@ -174,15 +184,20 @@ __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid
   }
 }
 
-// One token's K int32 entries: 16-byte stores when the row is whole (K ==
-// KMAX, a multiple of 4) and aligned, else one word per slot.
+// One token's K int32 entries: when K == KMAX, as whole-row pieces of w
+// words (16 or 8 bytes; w = 4 needs K % 4 == 0, w = 2 an even K), else one
+// word per slot.
 template <int KMAX>
-__device__ __forceinline__ void store_row(int32_t* dst, const int (&v)[KMAX], int K, bool vec) {
-  if (vec && K == KMAX && (KMAX % 4) == 0) {
+__device__ __forceinline__ void store_row(int32_t* dst, const int (&v)[KMAX], int K, int w) {
+  if (KMAX % 4 == 0 && K == KMAX && w == 4) {
 #pragma unroll
     for (int q = 0; q < KMAX / 4; ++q)
       reinterpret_cast<u32x4*>(dst)[q] = u32x4{uint32_t(v[4 * q]), uint32_t(v[4 * q + 1]),
                                                uint32_t(v[4 * q + 2]), uint32_t(v[4 * q + 3])};
+  } else if (KMAX % 2 == 0 && K == KMAX && w >= 2) {
+#pragma unroll
+    for (int q = 0; q < KMAX / 2; ++q)
+      reinterpret_cast<u32x2*>(dst)[q] = u32x2{uint32_t(v[2 * q]), uint32_t(v[2 * q + 1])};
   } else {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
@@ -245,11 +260,11 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
     const bool valid = t < a.T;
     decode<MODE, KMAX>(a, t, valid, sl);
     if (MODE == kFusedSend && valid) {
-      store_row<KMAX>(a.dest + t * a.K, sl.bin, a.K, a.vec_out);
-      // membership row: 16 destinations per 16-byte store when the rows
-      // allow it, else 4 per 32-bit store (P % 4 == 0) or bytes
+      store_row<KMAX>(a.dest + t * a.K, sl.bin, a.K, a.out_w);
+      // membership row: 16 or 8 destinations per store when the rows allow
+      // it, else 4 per 32-bit store (P % 4 == 0) or bytes
       uint8_t* row = a.is_in_rank + t * P;
-      const int step = a.vec_iir ? 16 : 4;
+      const int step = a.iir_w == 4 ? 16 : (a.iir_w == 2 ? 8 : 4);
       for (int p0 = 0; p0 < P; p0 += step) {
         uint32_t word[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -257,8 +272,10 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
           const int d = sl.bin[k] - p0;
           if (d >= 0 && d < step) word[d >> 2] |= 1u << (8 * (d & 3));
         }
-        if (a.vec_iir) {
+        if (a.iir_w == 4) {
           *reinterpret_cast<u32x4*>(row + p0) = u32x4{word[0], word[1], word[2], word[3]};
+        } else if (a.iir_w == 2) {
+          *reinterpret_cast<u32x2*>(row + p0) = u32x2{word[0], word[1]};
         } else if ((P & 3) == 0) {
           *reinterpret_cast<uint32_t*>(row + p0) = word[0];
         } else {
@@ -470,7 +487,7 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
         if (n < a.capacity) rowk[k] = int32_t(n);
       }
     }
-    if (valid) store_row<KMAX>(a.token_row + t * a.K, rowk, a.K, a.vec_out);
+    if (valid) store_row<KMAX>(a.token_row + t * a.K, rowk, a.K, a.out_w);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       bool first = sl.bin[k] >= 0 && rowk[k] >= 0;
@@ -501,12 +518,20 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
           iv[q] = own ? int32_t(sl.ids[kk + q] - ob) : -1;
           wv[q] = own ? sl.wts[kk + q] : 0.0f;
         }
-        if (a.vec_rows) {
+        if (KMAX % 4 == 0 && a.rows_w == 4) {
           *reinterpret_cast<u32x4*>(irow + kk) =
               u32x4{uint32_t(iv[0]), uint32_t(iv[1]), uint32_t(iv[2]), uint32_t(iv[3])};
           *reinterpret_cast<u32x4*>(wrow + kk) =
               u32x4{__float_as_uint(wv[0]), __float_as_uint(wv[1]), __float_as_uint(wv[2]),
                     __float_as_uint(wv[3])};
+        } else if (KMAX % 2 == 0 && a.K == KMAX && a.rows_w >= 2) {
+          *reinterpret_cast<u32x2*>(irow + kk) = u32x2{uint32_t(iv[0]), uint32_t(iv[1])};
+          *reinterpret_cast<u32x2*>(wrow + kk) = u32x2{__float_as_uint(wv[0]), __float_as_uint(wv[1])};
+          if (kk + 2 < KMAX) {
+            *reinterpret_cast<u32x2*>(irow + kk + 2) = u32x2{uint32_t(iv[2]), uint32_t(iv[3])};
+            *reinterpret_cast<u32x2*>(wrow + kk + 2) =
+                u32x2{__float_as_uint(wv[2]), __float_as_uint(wv[3])};
+          }
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -532,8 +557,14 @@ size_t fused_smem_bytes(int P, int E, int tiles_per_group, int waves) {
 
 template <int MODE, int NW>
 void launch_fused_nw(const FusedArgs& a, unsigned groups, size_t smem, hipStream_t s) {
-  if (a.K <= 4)
+  // K = 2 and 6 have instances of their own, so that every even K up to 8
+  // reads and writes whole rows (K == KMAX) without per-slot guards.
+  if (a.K <= 2)
+    dispatch_layout_kernel<MODE, 2, NW><<<groups, NW * kWave, smem, s>>>(a);
+  else if (a.K <= 4)
     dispatch_layout_kernel<MODE, 4, NW><<<groups, NW * kWave, smem, s>>>(a);
+  else if (a.K <= 6)
+    dispatch_layout_kernel<MODE, 6, NW><<<groups, NW * kWave, smem, s>>>(a);
   else if (a.K <= 8)
     dispatch_layout_kernel<MODE, 8, NW><<<groups, NW * kWave, smem, s>>>(a);
   else

@@ -94,6 +94,51 @@ def test_fused_layout_matches_oracle(T, E, K, P, routing, unrouted):
     check_fused(idx, w, P, E // P)
 
 
+@pytest.mark.parametrize("K,P,words", [(6, 8, 1), (6, 16, 2), (8, 32, 1), (8, 32, 2), (2, 2, 1),
+                                         (4, 16, 3)])
+def test_fused_layout_unaligned_rows(K, P, words):
+    """Arrays that start a few words past 16-byte alignment (views into
+    larger buffers) take the narrower whole-row accesses, or one word per
+    slot, and give the same results."""
+    T, El = 777, 4
+    idx, w = _case(T, P * El, K, P, seed=5)
+    cap = T * min(K, P)
+    print(f"case: unaligned K={K} P={P} offset={words} words", flush=True)
+
+    def at(shape, dtype, fill, k):
+        n = int(np.prod(shape))
+        return torch.full((n + k,), fill, dtype=dtype, device="cuda")[k:].view(shape)
+
+    d_idx = at((T, K), torch.int64, 0, 1)                # 8 bytes off
+    d_idx.copy_(to_dev(idx))
+    d_w = at((T, K), torch.float32, 0.0, words)
+    d_w.copy_(to_dev(w))
+    counts = ep.Counts(dest=at((T, K), torch.int32, -9, words),
+                       is_in_rank=at((T, P), torch.uint8, 9, 4 * words),
+                       send_counts=at((1, P), torch.int32, -9, words),
+                       tokens_per_expert=at((1, P * El), torch.int32, -9, words),
+                       diag=at((1,), torch.int32, -9, words))
+    lay = ep.SendLayout(send_token_idx=at((cap,), torch.int32, -7, words),
+                        send_rank=at((cap,), torch.int32, -7, words),
+                        send_idx=at((cap, K), torch.int32, -7, words),
+                        send_w=at((cap, K), torch.float32, -7.0, words),
+                        token_row=at((T, K), torch.int32, -7, words))
+    ep.ep_dispatch_layout(d_idx, d_w, P, El, cap, counts=counts, out=lay)
+    dest, iir, sc, tpe = O.compute_send_counts(idx, P, El, 1)
+    assert np.array_equal(host(counts.dest), dest)
+    assert np.array_equal(host(counts.is_in_rank), iir)
+    assert np.array_equal(host(counts.send_counts), sc)
+    assert np.array_equal(host(counts.tokens_per_expert), tpe)
+    sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, P, El)
+    N = len(sti)
+    assert np.array_equal(host(lay.send_token_idx)[:N], sti)
+    assert np.array_equal(host(lay.send_rank)[:N], srk)
+    assert np.array_equal(host(lay.send_idx)[:N], sidx)
+    assert np.array_equal(host(lay.send_w)[:N].view(np.uint32), sw.view(np.uint32))
+    assert np.array_equal(host(lay.token_row), trow)
+    assert np.all(host(lay.send_idx)[N:] == -7)
+
+
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_fused_layout_other_seeds(seed):
     idx, w = _case(4000, 256, 8, 32, "zipf", 0.05, seed=seed)
