@@ -608,9 +608,14 @@ void launch_permute_fp8_k(const RowArgs& a, hipStream_t s) {
 template <int KMAX>
 void launch_combine_k(const CombineArgs& a, hipStream_t s) {
   const int64_t H8 = a.H >> 3;
-  if (a.R < 2 * a.T) {
-    // Fewer than two rows per token on average: the sparse form, up to 7
-    // pieces per thread (a 7168-channel row in one workgroup).
+  // The sparse form, up to 7 pieces per thread (a 7168-channel row in one
+  // workgroup), keeps more bytes in flight when tokens read one or two rows:
+  // fewer than two rows per token, or more rows than the K*T slots can name
+  // (a padded buffer such as the expert-batched one, where a token reads
+  // only its local experts' rows: 50 against 93 us on the 8k-token batched
+  // combine).  Tokens that read many rows are faster in the dense form
+  // (312 against 360 us on the 16k-token send layout).
+  if (a.R < 2 * a.T || a.R > int64_t(a.K) * a.T) {
     const int per = int((H8 + kSparseBlock - 1) / kSparseBlock) < 7
                         ? int((H8 + kSparseBlock - 1) / kSparseBlock) : 7;
     const int64_t nch = (H8 + int64_t(kSparseBlock) * per - 1) / (int64_t(kSparseBlock) * per);

@@ -425,8 +425,7 @@ int ep_batched_prepare_fp8(const void* x, const int64_t* topk_idx,
  * are given are added after the expert terms, bias0 first; the sum is rounded
  * once to bf16, to nearest with ties to even (past the largest bf16: an
  * infinity; a NaN stays a quiet NaN, sign and payload unspecified).  Rows
- * r >= num_rows are
- * skipped.  Tokens with no row give +0 (plus the biases).
+ * r >= num_rows are skipped.  Tokens with no row give +0 (plus the biases).
  *
  *   y             [num_rows, H] bf16 in   expert outputs (send rows, or the
  *                                         batched buffer viewed as rows)
@@ -434,6 +433,12 @@ int ep_batched_prepare_fp8(const void* x, const int64_t* topk_idx,
  *   topk_weights  [T,K] fp32 in, or NULL for the unweighted partial sums
  *   bias0, bias1  [T,H] bf16 in, or NULL (16-byte aligned)
  *   out           [T,H] bf16 out
+ * The launch shape follows from num_rows, with the same results either way:
+ * when num_rows < 2T, or num_rows > K*T (a padded buffer such as the
+ * expert-batched one, whose tokens read only their local experts' rows), a
+ * workgroup walks a token's rows one after another with several 16-byte
+ * pieces per thread; otherwise it loads all of a token's rows at once, one
+ * piece per thread.
  */
 int ep_combine(const void* y, int64_t num_rows, const int32_t* token_row,
                const float* topk_weights, int64_t num_tokens, int num_topk,

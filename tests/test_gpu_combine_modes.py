@@ -88,3 +88,27 @@ def test_duplicate_rows_added_once_and_bias_only_tokens():
     ref = O.combine_partials(y, trow, biases=(b0,))
     assert np.array_equal(got, ref)
     assert np.array_equal(got[2], b0[2])        # no rows: the bias itself
+
+
+@pytest.mark.parametrize("T,H,E,K,P", [(1200, 7168, 256, 8, 32), (500, 1024, 64, 6, 8),
+                                       (300, 4096, 16, 16, 4)])
+def test_combine_launch_shapes_agree(T, H, E, K, P):
+    """The same send rows combined as a buffer of exactly the send rows
+    (R <= K*T: all of a token's rows loaded at once) and inside a larger
+    padded buffer (R > K*T: rows walked one after another): both equal the
+    oracle bit for bit, weighted and unweighted."""
+    idx, w, (sti, _, _, _, trow) = _layout(T, H, E, K, P, "zipf", 0.05, seed=4)
+    rng = np.random.default_rng(9)
+    N = len(sti)
+    y = _rand_bf16(rng, (N, H))
+    want_w = O.combine(y, trow, w)
+    want_u = O.combine_partials(y, trow)
+    pad = K * T + 5 - N                       # rows past the send rows, never named
+    assert pad > 0
+    y_big = np.concatenate([y, _rand_bf16(rng, (pad, H))])
+    print(f"case: launch shapes T={T} H={H} K={K} P={P} N={N} R={len(y_big)}", flush=True)
+    d_trow, d_w = to_dev(trow), to_dev(w)
+    for rows in (y, y_big):
+        d_y = to_dev(rows)
+        assert np.array_equal(bits(ep.ep_combine(d_y, d_trow, d_w)), want_w)
+        assert np.array_equal(bits(ep.ep_combine(d_y, d_trow, None)), want_u)
