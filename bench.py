@@ -12,11 +12,13 @@ routing, with inputs already resident in HBM:
 The identity expert sits between dispatch and combine: combine reads the send
 rows themselves (bf16), or the dequantized fp8 rows prepared before timing.
 
-Every step, warm-up included, follows a 512 MiB scratch read (outside the
-step's events) that clears the 256 MB Infinity Cache, so each step reads its
-inputs from HBM.  A read leaves the cache holding clean lines; a clearing
-write would leave up to 256 MB of dirty lines that the step itself would then
-have to write back.  ``--back-to-back`` times K uninterrupted steps instead.
+Every step, warm-up included, starts after a 512 MiB scratch read that clears
+the 256 MB Infinity Cache, so each step reads its inputs from HBM, and the
+cache holds only clean lines (a clearing write would leave up to 256 MB of
+its own dirty lines for the step to write back).  A step is charged for the
+lines it leaves dirty: its time runs to the end of the next clearing read,
+which writes them back, minus the time that read takes on a clean cache.
+``--back-to-back`` times K uninterrupted steps instead.
 
 Prints ONE JSON line.  ``value`` is algorithmic HBM bytes per step / step
 time (GB/s); tokens/s and the fraction of the 8 TB/s HBM peak ride along.
@@ -540,13 +542,30 @@ def traffic_from_profiles(workload, kernel_name, source_digest):
 
 class CacheClear:
     """Reads 512 MiB of device memory (a max over 128 Mi floats), which
-    evicts everything the 256 MB Infinity Cache held and leaves it clean."""
+    evicts everything the 256 MB Infinity Cache held and leaves it clean;
+    lines left dirty before it are written back during it."""
 
     def __init__(self, torch, dev):
+        self.torch = torch
         self.buf = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
 
     def run(self):
         self.buf.max()
+
+    def clean_ms(self, stream, n=12):
+        """Median time of the read on an already clean cache."""
+        t = self.torch
+        self.run()
+        ts = []
+        for _ in range(n):
+            e0 = t.cuda.Event(enable_timing=True)
+            e1 = t.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            self.run()
+            e1.record(stream)
+            t.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
 
 
 def main():
@@ -643,18 +662,26 @@ def main():
         ms = ev0.elapsed_time(ev1) / args.steps
         step_ms = [ms]
     else:
-        # Each step between its own events, the cache-clearing read before it.
+        # Each step starts on a cleared cache and is charged for the lines it
+        # leaves dirty: its interval runs from before the step to after the
+        # next clearing read, which writes those lines back, and the time the
+        # same read takes on a clean cache is subtracted.
+        clear_ms = scratch.clean_ms(main_stream)
+        scratch.run()
         evs = []
         for _ in range(args.steps):
-            scratch.run()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            e2 = torch.cuda.Event(enable_timing=True)
             e0.record(main_stream)
             step()
             e1.record(main_stream)
-            evs.append((e0, e1))
+            scratch.run()
+            e2.record(main_stream)
+            evs.append((e0, e1, e2))
         torch.cuda.synchronize()
-        step_ms = [a.elapsed_time(b) for a, b in evs]
+        step_ms = [a.elapsed_time(c) - clear_ms for a, _, c in evs]
+        events_ms = [a.elapsed_time(b) for a, b, _ in evs]
         ms = float(np.mean(step_ms))
     wall = time.perf_counter() - w0
     log(f"[bench] {args.steps} timed steps: {ms:.4f} ms/step (events), "
@@ -706,8 +733,12 @@ def main():
         "alg_bytes_per_step": total_bytes,
         "wall_ms_per_step": round(1000 * wall / args.steps, 5),
         "step_timing": ("one event pair around K back-to-back steps" if args.back_to_back else
-                        "events around each step; a 512 MiB cache-clearing read precedes "
-                        "every step, outside its events (wall time includes it)"),
+                        "each step starts on a cache cleared by a 512 MiB read; its time "
+                        "runs to the end of the next clearing read (which writes back the "
+                        "lines the step left dirty) minus that read's time on a clean cache"),
+        **({} if args.back_to_back else {
+            "clean_clear_ms": round(clear_ms, 5),
+            "ms_per_step_to_last_kernel": round(float(np.mean(events_ms)), 5)}),
         "kernel_avg_us": {k: round(v, 3) for k, v in kern_us.items()},
         "roofline": {
             "kernel": dom,
