@@ -122,17 +122,19 @@ const char* ep_status_string(int status) {
 size_t ep_counts_workspace_bytes(int64_t num_tokens, int num_ranks, int num_local_experts,
                                  int num_chunks) {
   if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1 || num_chunks < 1) return 0;
+  if (num_tokens >= kMaxTokens || int64_t(num_ranks) * num_local_experts > kMaxExperts) return 0;
   return count_ws_bytes(num_ranks, num_ranks * num_local_experts, num_chunks);
 }
 
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_bins) {
-  if (num_tokens < 0 || num_bins < 1) return 0;
+  if (num_tokens < 0 || num_tokens >= kMaxTokens || num_bins < 1) return 0;
   return kWsHeaderBytes + scan_status_bytes(num_tokens, num_bins);
 }
 
 size_t ep_batched_workspace_bytes(int64_t num_tokens, int num_local_experts,
                                   int64_t max_num_tokens) {
-  if (num_tokens < 0 || num_local_experts < 1 || max_num_tokens < 0) return 0;
+  if (num_tokens < 0 || num_tokens >= kMaxTokens || num_local_experts < 1 || max_num_tokens < 0)
+    return 0;
   return kWsHeaderBytes + scan_status_bytes(num_tokens, num_local_experts);
 }
 
@@ -219,6 +221,7 @@ int ep_build_send_layout(const int64_t* topk_idx, const float* topk_weights, con
 size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
                                           int num_local_experts) {
   if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1) return 0;
+  if (num_tokens >= kMaxTokens || int64_t(num_ranks) * num_local_experts > kMaxExperts) return 0;
   const int64_t nh = int64_t(num_ranks) + int64_t(num_ranks) * num_local_experts + 1;
   return fused_ws_bytes(num_tokens, num_ranks, nh);
 }
@@ -284,7 +287,7 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
 }
 
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins) {
-  if (num_rows < 0 || num_bins < 1) return 0;
+  if (num_rows < 0 || num_rows >= kMaxTokens || num_bins < 1) return 0;
   return fused_ws_bytes(num_rows, num_bins, int64_t(num_bins) + 1);
 }
 
@@ -409,7 +412,7 @@ int ep_batched_prepare(const void* x, const int64_t* topk_idx, int64_t num_token
   if (num_tokens >= kMaxTokens || num_topk > EPDC_MAX_TOPK ||
       num_local_experts > EPDC_MAX_BINS || num_tokens * num_topk > INT32_MAX)
     return EP_ERR_UNSUPPORTED;
-  if (int64_t(num_local_experts) * max_num_tokens > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  if (max_num_tokens > INT32_MAX / num_local_experts) return EP_ERR_UNSUPPORTED;  // E_local*max
   int st = check_hidden(hidden, false);
   if (st != EP_OK) return st;
   if (!arr_ok(x, num_tokens, 16) || !arr_ok(topk_idx, num_tokens, 8) ||
@@ -471,7 +474,7 @@ int ep_batched_prepare_fp8(const void* x, const int64_t* topk_idx, int64_t num_t
   if (num_tokens >= kMaxTokens || num_topk > EPDC_MAX_TOPK ||
       num_local_experts > EPDC_MAX_BINS || num_tokens * num_topk > INT32_MAX)
     return EP_ERR_UNSUPPORTED;
-  if (int64_t(num_local_experts) * max_num_tokens > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  if (max_num_tokens > INT32_MAX / num_local_experts) return EP_ERR_UNSUPPORTED;  // E_local*max
   int st = check_hidden(hidden, true);
   if (st != EP_OK) return st;
   const bool ue8m0 = scale_fmt == EP_SCALE_UE8M0;

@@ -53,7 +53,9 @@
  *    ep_batched_prepare, ep_batched_prepare_fp8); or the one-launch layouts
  *    (ep_dispatch_layout, ep_regroup_by_expert).  Zero it once, size it for
  *    the largest call, and do not hand it to a call of another family or to
- *    two calls that may run at the same time.
+ *    two calls that may run at the same time.  The ep_*_workspace_bytes
+ *    functions return 0 for negative or zero sizes and for T >= 2^30 or
+ *    E > 8192, which the calls reject before they look at a workspace.
  */
 #ifndef EPDC_H
 #define EPDC_H

@@ -59,6 +59,25 @@ def test_workspace_sizes():
     assert L.ep_batched_workspace_bytes(8192, 0, 8192) == 0
 
 
+def test_workspace_sizes_past_the_limits_are_zero():
+    # sizes every call rejects (T >= 2^30, E > 8192) give 0, with no
+    # arithmetic overflow on the way (INT64_MAX tokens, 2^16 x 2^16 experts)
+    L = _lib.lib()
+    big = (1 << 63) - 1
+    for T in (1 << 30, big):
+        assert L.ep_counts_workspace_bytes(T, 32, 8, 1) == 0
+        assert L.ep_layout_workspace_bytes(T, 32) == 0
+        assert L.ep_batched_workspace_bytes(T, 32, 8192) == 0
+        assert L.ep_dispatch_layout_workspace_bytes(T, 32, 8) == 0
+        assert L.ep_regroup_workspace_bytes(T, 256) == 0
+    assert L.ep_counts_workspace_bytes(16, 1 << 16, 1 << 16, 1) == 0
+    assert L.ep_dispatch_layout_workspace_bytes(16, 1 << 16, 1 << 16) == 0
+    assert L.ep_counts_workspace_bytes(16, 1024, 8, 1) == 256 + (1024 + 8192 + 1) * 4
+    assert L.ep_counts_workspace_bytes(16, 1024, 9, 1) == 0
+    # the largest supported token count still gets a size
+    assert L.ep_layout_workspace_bytes((1 << 30) - 1, 2) == 256 + (1 << 22) * 2 * 8
+
+
 # Host-side validation: every call below returns before any HIP call, because
 # an argument is rejected.  Pointers are fake but never dereferenced.
 P = ctypes.c_void_p
@@ -187,6 +206,8 @@ def test_batched_rejects_bad_arguments():
     assert call(El=0) == _lib.EP_ERR_INVALID_ARG
     assert call(El=2000) == _lib.EP_ERR_UNSUPPORTED
     assert call(M=1 << 30) == _lib.EP_ERR_UNSUPPORTED
+    # E_local * max past int64 (it once wrapped negative and passed the check)
+    assert call(El=128, M=(1 << 63) - 1) == _lib.EP_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.EP_ERR_WORKSPACE
 
 
@@ -203,6 +224,7 @@ def test_batched_fp8_rejects_bad_arguments():
     assert call(first=-1) == _lib.EP_ERR_INVALID_ARG
     assert call(El=2000) == _lib.EP_ERR_UNSUPPORTED
     assert call(M=1 << 30) == _lib.EP_ERR_UNSUPPORTED
+    assert call(El=128, M=(1 << 63) - 1) == _lib.EP_ERR_UNSUPPORTED
     assert call(q=A8) == _lib.EP_ERR_INVALID_ARG
     assert call(sc=None) == _lib.EP_ERR_INVALID_ARG
     assert call(sc=ODD) == _lib.EP_ERR_INVALID_ARG
