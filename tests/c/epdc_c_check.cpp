@@ -1,7 +1,7 @@
 // The send path through the C ABI with nothing but the HIP runtime: device
 // buffers from hipMalloc, a zero-filled workspace, the default stream, no
 // PyTorch.  Reads a case file, runs counts + layout in one launch, the bf16
-// permute and the weighted combine, checks that an invalid call is refused
+// permute, the weighted combine and the fp8 permute, checks that an invalid call is refused
 // before anything is enqueued, and writes what the calls produced for the
 // caller to compare with the CPU oracle.
 //
@@ -9,7 +9,8 @@
 //   CASE: int64 T, K, P, E_local, H; int64 topk_idx[T*K]; float w[T*K];
 //         uint16 x[T*H] (bf16 bits)
 //   OUT:  int64 N; int32 send_counts[P]; int32 token_row[T*K];
-//         int32 send_token_idx[N]; uint16 send_x[N*H]; uint16 out[T*H]
+//         int32 send_token_idx[N]; uint16 send_x[N*H]; uint16 out[T*H];
+//         uint8 send_q[N*H]; float send_scale[N*H/128]   (H a multiple of 128)
 // Exit status 0 on success; 1 usage or file, 2 HIP, 3 library status,
 // 4 ABI version, 5 an invalid call was accepted.
 #include <hip/hip_runtime.h>
@@ -58,7 +59,7 @@ int main(int argc, char** argv) {
   if (std::fread(h, sizeof(int64_t), 5, f) != 5) return 1;
   const int64_t T = h[0];
   const int K = int(h[1]), P = int(h[2]), El = int(h[3]), H = int(h[4]);
-  if (T < 1 || K < 1 || P < 1 || El < 1 || H < 8) return 1;
+  if (T < 1 || K < 1 || P < 1 || El < 1 || H < 128 || H % 128 != 0) return 1;
   const int64_t TK = T * K, cap = T * (K < P ? K : P);
   std::vector<int64_t> idx(TK);
   std::vector<float> w(TK);
@@ -69,6 +70,8 @@ int main(int argc, char** argv) {
   int64_t* d_idx;
   float *d_w, *d_sw;
   uint16_t *d_x, *d_sx, *d_out;
+  uint8_t* d_q;
+  float* d_qs;
   int32_t *d_dest, *d_sc, *d_tpe, *d_diag, *d_sti, *d_srk, *d_sidx, *d_trow;
   uint8_t* d_iir;
   void* d_ws;
@@ -88,6 +91,8 @@ int main(int argc, char** argv) {
   HIP_CHECK(hipMalloc(&d_trow, TK * 4));
   HIP_CHECK(hipMalloc(&d_sx, size_t(cap) * H * 2));
   HIP_CHECK(hipMalloc(&d_out, size_t(T) * H * 2));
+  HIP_CHECK(hipMalloc(&d_q, size_t(cap) * H));
+  HIP_CHECK(hipMalloc(&d_qs, size_t(cap) * (H / 128) * 4));
   HIP_CHECK(hipMalloc(&d_ws, ws));
   HIP_CHECK(hipMemset(d_ws, 0, ws));
   HIP_CHECK(hipMemcpy(d_idx, idx.data(), TK * sizeof(int64_t), hipMemcpyHostToDevice));
@@ -99,6 +104,7 @@ int main(int argc, char** argv) {
   EP_CHECK(ep_dispatch_permute(d_x, T, H, d_trow, K, cap, EP_DTYPE_BF16, d_sx, nullptr,
                                nullptr));
   EP_CHECK(ep_combine(d_sx, cap, d_trow, d_w, T, K, H, nullptr, nullptr, d_out, nullptr));
+  EP_CHECK(ep_dispatch_permute(d_x, T, H, d_trow, K, cap, EP_DTYPE_FP8_E4M3, d_q, d_qs, nullptr));
   // refused on the host, before anything is enqueued: no output buffer
   if (ep_combine(d_sx, cap, d_trow, d_w, T, K, H, nullptr, nullptr, nullptr, nullptr) !=
       EP_ERR_INVALID_ARG)
@@ -107,11 +113,15 @@ int main(int argc, char** argv) {
 
   std::vector<int32_t> sc(P), trow(TK), sti(cap);
   std::vector<uint16_t> sx(size_t(cap) * H), out(size_t(T) * H);
+  std::vector<uint8_t> q(size_t(cap) * H);
+  std::vector<float> qs(size_t(cap) * (H / 128));
   HIP_CHECK(hipMemcpy(sc.data(), d_sc, size_t(P) * 4, hipMemcpyDeviceToHost));
   HIP_CHECK(hipMemcpy(trow.data(), d_trow, TK * 4, hipMemcpyDeviceToHost));
   HIP_CHECK(hipMemcpy(sti.data(), d_sti, cap * 4, hipMemcpyDeviceToHost));
   HIP_CHECK(hipMemcpy(sx.data(), d_sx, size_t(cap) * H * 2, hipMemcpyDeviceToHost));
   HIP_CHECK(hipMemcpy(out.data(), d_out, size_t(T) * H * 2, hipMemcpyDeviceToHost));
+  HIP_CHECK(hipMemcpy(q.data(), d_q, q.size(), hipMemcpyDeviceToHost));
+  HIP_CHECK(hipMemcpy(qs.data(), d_qs, qs.size() * 4, hipMemcpyDeviceToHost));
   int64_t N = 0;
   for (int p = 0; p < P; ++p) N += sc[p];
   if (N > cap) return 3;
@@ -120,11 +130,13 @@ int main(int argc, char** argv) {
   if (!g) return 1;
   const bool ok = write_all(g, &N, 1) && write_all(g, sc.data(), sc.size()) &&
                   write_all(g, trow.data(), trow.size()) && write_all(g, sti.data(), size_t(N)) &&
-                  write_all(g, sx.data(), size_t(N) * H) && write_all(g, out.data(), out.size());
+                  write_all(g, sx.data(), size_t(N) * H) && write_all(g, out.data(), out.size()) &&
+                  write_all(g, q.data(), size_t(N) * H) && write_all(g, qs.data(), size_t(N) * (H / 128));
   std::fclose(g);
   for (void* p : {(void*)d_idx, (void*)d_w, (void*)d_x, (void*)d_dest, (void*)d_iir, (void*)d_sc,
                   (void*)d_tpe, (void*)d_diag, (void*)d_sti, (void*)d_srk, (void*)d_sidx,
-                  (void*)d_sw, (void*)d_trow, (void*)d_sx, (void*)d_out, d_ws})
+                  (void*)d_sw, (void*)d_trow, (void*)d_sx, (void*)d_out, (void*)d_q, (void*)d_qs,
+                  d_ws})
     HIP_CHECK(hipFree(p));
   return ok ? 0 : 1;
 }

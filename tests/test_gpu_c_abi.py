@@ -1,5 +1,5 @@
 """The C ABI on its own: tests/c/epdc_c_check.cpp drives counts + layout, the
-bf16 permute and the weighted combine with nothing but the HIP runtime (no
+bf16 and fp8 permutes and the weighted combine with nothing but the HIP runtime (no
 PyTorch in that process), and its outputs match the CPU oracle bit for bit.
 It also checks the ABI version and that an invalid call is refused."""
 
@@ -44,8 +44,10 @@ def _read_out(path, T, K, P, H):
     sti = take(np.int32, N)
     sx = take(np.uint16, N * H).reshape(N, H)
     out = take(np.uint16, T * H).reshape(T, H)
+    q = take(np.uint8, N * H).reshape(N, H)
+    qs = take(np.float32, N * (H // 128)).reshape(N, H // 128)
     assert off == len(buf)
-    return sc, trow, sti, sx, out
+    return sc, trow, sti, sx, out, q, qs
 
 
 @pytest.mark.parametrize("name,T,H", [("tiny", 256, 512), ("skewed_t16384", 3000, 2048),
@@ -62,7 +64,7 @@ def test_c_program_matches_oracle(tmp_path, name, T, H):
     proc = subprocess.run([CHECK, str(case), str(out)], capture_output=True, text=True,
                           timeout=60, close_fds=True)
     assert proc.returncode == 0, (proc.returncode, proc.stderr)
-    sc, trow, sti, sx, got = _read_out(out, s.T, s.K, s.P, s.H)
+    sc, trow, sti, sx, got, q, qs = _read_out(out, s.T, s.K, s.P, s.H)
 
     _, _, osc, _ = O.compute_send_counts(idx, s.P, s.E_local)
     osti, _, _, _, otrow = O.build_send_layout(idx, w, s.P, s.E_local)
@@ -71,3 +73,6 @@ def test_c_program_matches_oracle(tmp_path, name, T, H):
     assert np.array_equal(trow, otrow)
     assert np.array_equal(sx, O.dispatch_permute(x, osti))
     assert np.array_equal(got, O.combine(O.dispatch_permute(x, osti), otrow, w))
+    oq, oqs = O.dispatch_permute_fp8(x, osti)
+    assert np.array_equal(q, oq)
+    assert np.array_equal(qs.view(np.uint32), oqs.view(np.uint32))
