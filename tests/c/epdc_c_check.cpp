@@ -11,10 +11,13 @@
 //   OUT:  int64 N; int32 send_counts[P]; int32 token_row[T*K];
 //         int32 send_token_idx[N]; uint16 send_x[N*H]; uint16 out[T*H];
 //         uint8 send_q[N*H]; float send_scale[N*H/128]   (H a multiple of 128)
-// Exit status 0 on success; 1 usage or file, 2 HIP, 3 library status,
-// 4 ABI version, 5 an invalid call was accepted.
+// It then captures the send path into a HIP graph and checks three replays
+// against the eager results.  Exit status 0 on success; 1 usage or file,
+// 2 HIP, 3 library status, 4 ABI version, 5 an invalid call was accepted,
+// 6 a graph replay differed.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <vector>
@@ -125,6 +128,42 @@ int main(int argc, char** argv) {
   int64_t N = 0;
   for (int p = 0; p < P; ++p) N += sc[p];
   if (N > cap) return 3;
+
+  // The same send path captured into a HIP graph on a stream of its own and
+  // replayed three times; its outputs are overwritten between the replays
+  // (outside the capture), and each replay must give the eager results again.
+  {
+    hipStream_t cs;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    HIP_CHECK(hipStreamCreate(&cs));
+    HIP_CHECK(hipStreamBeginCapture(cs, hipStreamCaptureModeGlobal));
+    int st1 = ep_dispatch_layout(d_idx, d_w, T, K, P, El, cap, d_dest, d_iir, d_sc, d_tpe, d_diag,
+                                 d_sti, d_srk, d_sidx, d_sw, d_trow, d_ws, ws, cs);
+    int st2 = ep_dispatch_permute(d_x, T, H, d_trow, K, cap, EP_DTYPE_BF16, d_sx, nullptr, cs);
+    int st3 = ep_combine(d_sx, cap, d_trow, d_w, T, K, H, nullptr, nullptr, d_out, cs);
+    HIP_CHECK(hipStreamEndCapture(cs, &graph));
+    if (st1 != EP_OK || st2 != EP_OK || st3 != EP_OK) return 3;
+    HIP_CHECK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+    std::vector<int32_t> trow2(TK);
+    std::vector<uint16_t> sx2(size_t(N) * H), out2(size_t(T) * H);
+    for (int rep = 0; rep < 3; ++rep) {
+      HIP_CHECK(hipMemset(d_trow, 0xFF, TK * 4));
+      HIP_CHECK(hipMemset(d_sx, 0xFF, size_t(cap) * H * 2));
+      HIP_CHECK(hipMemset(d_out, 0xFF, size_t(T) * H * 2));
+      HIP_CHECK(hipDeviceSynchronize());
+      HIP_CHECK(hipGraphLaunch(exec, cs));
+      HIP_CHECK(hipStreamSynchronize(cs));
+      HIP_CHECK(hipMemcpy(trow2.data(), d_trow, TK * 4, hipMemcpyDeviceToHost));
+      HIP_CHECK(hipMemcpy(sx2.data(), d_sx, size_t(N) * H * 2, hipMemcpyDeviceToHost));
+      HIP_CHECK(hipMemcpy(out2.data(), d_out, size_t(T) * H * 2, hipMemcpyDeviceToHost));
+      if (trow2 != trow || !std::equal(sx2.begin(), sx2.end(), sx.begin()) || out2 != out)
+        return 6;
+    }
+    HIP_CHECK(hipGraphExecDestroy(exec));
+    HIP_CHECK(hipGraphDestroy(graph));
+    HIP_CHECK(hipStreamDestroy(cs));
+  }
 
   std::FILE* g = std::fopen(argv[2], "wb");
   if (!g) return 1;

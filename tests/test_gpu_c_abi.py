@@ -1,7 +1,8 @@
 """The C ABI on its own: tests/c/epdc_c_check.cpp drives counts + layout, the
 bf16 and fp8 permutes and the weighted combine with nothing but the HIP runtime (no
 PyTorch in that process), and its outputs match the CPU oracle bit for bit.
-It also checks the ABI version and that an invalid call is refused."""
+It also checks the ABI version, that an invalid call is refused, and that
+the send path captured into a HIP graph replays to the eager results."""
 
 import os
 import subprocess
