@@ -56,6 +56,10 @@ _SIGNATURES = {
 _lib = None
 
 
+# EPDC_ABI_VERSION of include/epdc.h that the signatures above follow
+ABI_VERSION = 3
+
+
 def header_functions():
     """Names of the functions declared in include/epdc.h."""
     with open(HEADER) as f:
@@ -77,6 +81,10 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if L.ep_abi_version() != ABI_VERSION:
+            raise ImportError(
+                f"{LIB_PATH} reports ABI version {L.ep_abi_version()}, these bindings are for "
+                f"{ABI_VERSION}: rebuild it with `python -m combine_ep_send_amd.build`")
         _lib = L
     return _lib
 

@@ -36,6 +36,12 @@ def test_library_exports_every_header_function():
     assert EXPECTED <= exported
 
 
+def test_bindings_follow_the_header_version():
+    import re
+    text = open(_lib.HEADER).read()
+    assert int(re.search(r"#define EPDC_ABI_VERSION (\d+)", text).group(1)) == _lib.ABI_VERSION
+
+
 def test_version_and_status_strings():
     # version 3: ep_batched_prepare_fp8 and the scale formats
     L = _lib.lib()
