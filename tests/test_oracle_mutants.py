@@ -13,6 +13,7 @@ import types
 import numpy as np
 import pytest
 
+import tests.test_oracle_fp8_rows as FR
 import tests.test_oracle_nonfinite as NF
 import tests.test_oracle_numerics as NUM
 import tests.test_oracle_routing as RT
@@ -90,6 +91,13 @@ NONFINITE_PINS = [
     pin(NF, "test_nan_elements_do_not_move_amax"),
     pin(NF, "test_all_nan_group_keeps_its_nans"),
     pin(NF, "test_infinite_group_gets_an_infinite_scale"),
+]
+FP8_ROW_PINS = [
+    pin(FR, "test_dequantize_matches_torch_decode_times_scale"),
+    pin(FR, "test_dequantize_hand_row"),
+    pin(FR, "test_dequantize_rounds_the_float32_product_once_to_bf16"),
+    pin(FR, "test_dispatch_permute_fp8_is_each_send_row_quantized"),
+    pin(FR, "test_dispatch_permute_fp8_follows_any_row_order"),
 ]
 BATCHED_PINS = [
     pin(RT, "test_batched_equals_stable_argsort", 0, 32),
@@ -223,6 +231,27 @@ MUTANTS = {
     "batched_fp8_padding_scale_one": (
         "    b_scale = np.zeros((El, M, sc.shape[1]), dtype=sc.dtype)",
         "    b_scale = np.ones((El, M, sc.shape[1]), dtype=sc.dtype)", SCALE_PINS),
+    "dequant_scale_of_neighbouring_group": (
+        "prod = (vals * np.asarray(scales, dtype=np.float32)[:, :, None]).astype(np.float32)",
+        "prod = (vals * np.roll(np.asarray(scales, dtype=np.float32), 1, axis=1)[:, :, None])"
+        ".astype(np.float32)", FP8_ROW_PINS),
+    "dequant_scale_rounded_to_bf16_first": (
+        "prod = (vals * np.asarray(scales, dtype=np.float32)[:, :, None]).astype(np.float32)",
+        "prod = (vals * bf16_to_f32(f32_to_bf16(np.asarray(scales, dtype=np.float32)))"
+        "[:, :, None]).astype(np.float32)", FP8_ROW_PINS),
+    "dequant_sign_dropped": (
+        "vals = e4m3_decode(q).astype(np.float32)",
+        "vals = np.abs(e4m3_decode(q)).astype(np.float32)", FP8_ROW_PINS),
+    "dequant_groups_interleaved": (
+        "vals = e4m3_decode(q).astype(np.float32).reshape(R, H // FP8_GROUP, FP8_GROUP)",
+        "vals = e4m3_decode(q).astype(np.float32).reshape(R, FP8_GROUP, H // FP8_GROUP)"
+        ".transpose(0, 2, 1)", FP8_ROW_PINS),
+    "permute_fp8_gathers_by_row_not_token": (
+        "rows = np.asarray(send_token_idx, dtype=np.int64)",
+        "rows = np.arange(len(send_token_idx), dtype=np.int64) % len(q)", FP8_ROW_PINS),
+    "permute_fp8_scales_of_another_row": (
+        "return q[rows].copy(), s[rows].copy()",
+        "return q[rows].copy(), s[np.sort(rows)].copy()", FP8_ROW_PINS),
     "batched_slots_descending": (
         "tokens = np.flatnonzero(hit_slots.any(axis=1))",
         "tokens = np.flatnonzero(hit_slots.any(axis=1))[::-1]", BATCHED_PINS),
@@ -252,6 +281,6 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 def test_unmutated_copy_passes_all_pins(monkeypatch):
     mod = make_mutant("FP8_GROUP = 128", "FP8_GROUP = 128")
     for module, fn, args in (ROUTING_PINS + COMBINE_PINS + FORMAT_PINS + BATCHED_PINS +
-                             PARTIAL_PINS + REGROUP_PINS + SCALE_PINS):
+                             PARTIAL_PINS + REGROUP_PINS + SCALE_PINS + FP8_ROW_PINS):
         monkeypatch.setattr(module, "O", mod)
         getattr(module, fn)(*args)
