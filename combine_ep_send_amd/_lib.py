@@ -15,6 +15,7 @@ EP_ERR_INVALID_ARG = -1
 EP_ERR_UNSUPPORTED = -2
 EP_ERR_WORKSPACE = -3
 EP_ERR_LAUNCH = -4
+EP_WS_WAIT_GAVE_UP = 1
 EP_DTYPE_BF16 = 0
 EP_DTYPE_FP8_E4M3 = 1
 EP_SCALE_F32 = 0
@@ -29,6 +30,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "ep_abi_version": (_I32, []),
     "ep_status_string": (ctypes.c_char_p, [_I32]),
+    "ep_workspace_status": (_I32, [_P, _SZ, _P, _P]),
     "ep_counts_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
     "ep_layout_workspace_bytes": (_SZ, [_I64, _I32]),
     "ep_batched_workspace_bytes": (_SZ, [_I64, _I32, _I64]),
@@ -57,7 +59,7 @@ _lib = None
 
 
 # EPDC_ABI_VERSION of include/epdc.h that the signatures above follow
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def header_functions():
@@ -77,14 +79,21 @@ def lib():
                 f"{LIB_PATH} is missing: build it with `python -m combine_ep_send_amd.build` "
                 "(there is no fallback implementation)")
         L = ctypes.CDLL(LIB_PATH)
+        # the version first: a library of another version may lack symbols
+        # these bindings name
+        try:
+            ver = L.ep_abi_version
+        except AttributeError:
+            raise ImportError(f"{LIB_PATH} exports no ep_abi_version: not an epdc library")
+        ver.restype, ver.argtypes = _I32, []
+        if ver() != ABI_VERSION:
+            raise ImportError(
+                f"{LIB_PATH} reports ABI version {ver()}, these bindings are for "
+                f"{ABI_VERSION}: rebuild it with `python -m combine_ep_send_amd.build`")
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.ep_abi_version() != ABI_VERSION:
-            raise ImportError(
-                f"{LIB_PATH} reports ABI version {L.ep_abi_version()}, these bindings are for "
-                f"{ABI_VERSION}: rebuild it with `python -m combine_ep_send_amd.build`")
         _lib = L
     return _lib
 

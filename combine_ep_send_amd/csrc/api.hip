@@ -119,6 +119,14 @@ const char* ep_status_string(int status) {
   }
 }
 
+int ep_workspace_status(void* workspace, size_t workspace_bytes, int32_t* flags,
+                        hipStream_t stream) {
+  if (!flags || !aligned(flags, 4)) return EP_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kWsHeaderBytes)
+    return EP_ERR_WORKSPACE;
+  return launch_status(launch_workspace_status(static_cast<uint32_t*>(workspace), flags, stream));
+}
+
 size_t ep_counts_workspace_bytes(int64_t num_tokens, int num_ranks, int num_local_experts,
                                  int num_chunks) {
   if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1 || num_chunks < 1) return 0;
@@ -305,7 +313,12 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
       num_rows * num_topk > INT32_MAX)
     return EP_ERR_UNSUPPORTED;
   const int bins = int(bins64);
-  if (capacity > INT32_MAX || int64_t(align) * bins > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  // Every regrouped row index, padding included, must fit int32: the rows
+  // number at most R*min(K, E_local) (one per distinct local id of a row)
+  // plus fewer than `align` padding rows per bin.
+  const int64_t most_rows = num_rows * (num_topk < num_local_experts ? num_topk : num_local_experts) +
+                            bins64 * (int64_t(align) - 1);
+  if (capacity > INT32_MAX || most_rows > INT32_MAX) return EP_ERR_UNSUPPORTED;
   int st = check_hidden(hidden, false);
   if (st != EP_OK) return st;
   const int64_t RK = num_rows * num_topk;

@@ -339,8 +339,9 @@ __global__ __launch_bounds__(kBlock) void scale_pad_kernel(ScalePadArgs a) {
 __global__ __launch_bounds__(kBlock) void regroup_pad_kernel(RegroupPadArgs a) {
   const int e = blockIdx.y;
   const int64_t H8 = a.H >> 3;
-  const int64_t start = int64_t(a.offsets[e]) + a.counts[e];
+  int64_t start = int64_t(a.offsets[e]) + a.counts[e];
   int64_t end = a.offsets[e + 1];
+  if (start < 0) start = 0;
   if (end > a.capacity) end = a.capacity;
   const int64_t n = (end - start) * H8;
   u32x4* px = static_cast<u32x4*>(a.perm_x);

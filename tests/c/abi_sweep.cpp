@@ -48,6 +48,14 @@ int main(int argc, char** argv) {
     std::fprintf(stderr, "usage: %s SEED ITERS\n", argv[0]);
     return 1;
   }
+  // The calls that pass validation launch kernels on fake pointers, which
+  // only a machine without a GPU refuses harmlessly: never run with one.
+  int devices = 0;
+  if (hipGetDeviceCount(&devices) == hipSuccess && devices > 0) {
+    std::fprintf(stderr, "abi_sweep: %d GPU(s) visible; this sweep runs only without a GPU\n",
+                 devices);
+    return 2;
+  }
   rng.seed(std::strtoull(argv[1], nullptr, 10));
   const long iters = std::strtol(argv[2], nullptr, 10);
   long rejected = 0, passed = 0;

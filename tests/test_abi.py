@@ -14,7 +14,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libepdc.so not built")
 
 EXPECTED = {
-    "ep_abi_version", "ep_status_string", "ep_counts_workspace_bytes", "ep_layout_workspace_bytes",
+    "ep_abi_version", "ep_status_string", "ep_workspace_status", "ep_counts_workspace_bytes", "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
     "ep_dispatch_layout_workspace_bytes", "ep_dispatch_layout",
     "ep_regroup_workspace_bytes", "ep_regroup_by_expert",
@@ -43,9 +43,9 @@ def test_bindings_follow_the_header_version():
 
 
 def test_version_and_status_strings():
-    # version 3: ep_batched_prepare_fp8 and the scale formats
+    # version 4: ep_workspace_status
     L = _lib.lib()
-    assert L.ep_abi_version() == 3
+    assert L.ep_abi_version() == 4
     assert L.ep_status_string(0) == b"ok"
     for s in (-1, -2, -3, -4):
         assert L.ep_status_string(s) not in (b"ok", b"unknown status")
@@ -182,6 +182,16 @@ def test_regroup_workspace_and_arguments():
     assert call(El=2000) == _lib.EP_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.EP_ERR_WORKSPACE
     assert call(ws_bytes=8) == _lib.EP_ERR_WORKSPACE
+    # Every regrouped row index, padding included, must fit int32: at most
+    # R*min(K, E_local) rows plus align-1 padding rows per bin.  1023 bins at
+    # align 2^21 leave room for exactly 2098174 one-slot rows; one more row
+    # is refused before the workspace is looked at (no launch either way).
+    big = dict(K=1, El=1, G=1023, grp=A16, align=1 << 21, ws=None)
+    fit = 2**31 - 1 - 1023 * ((1 << 21) - 1)
+    assert fit == 2098174
+    assert call(R=fit, **big) == _lib.EP_ERR_WORKSPACE
+    assert call(R=fit + 1, **big) == _lib.EP_ERR_UNSUPPORTED
+    assert call(R=(1 << 23) + 1, **big) == _lib.EP_ERR_UNSUPPORTED
 
 
 def test_permute_and_combine_reject_bad_rows():
@@ -236,3 +246,22 @@ def test_batched_fp8_rejects_bad_arguments():
     assert call(sc=ODD) == _lib.EP_ERR_INVALID_ARG
     assert call(ws=None) == _lib.EP_ERR_WORKSPACE
     assert call(ws_bytes=16) == _lib.EP_ERR_WORKSPACE
+
+
+def test_loader_checks_the_version_before_binding_symbols(tmp_path, monkeypatch):
+    # a stub that exports only ep_abi_version, reporting an older version:
+    # the loader must name the mismatch, not fail on a missing symbol
+    src = tmp_path / "stub.c"
+    src.write_text("int ep_abi_version(void) { return 2; }\n")
+    so = tmp_path / "libepdc.so"
+    subprocess.run(["gcc", "-shared", "-fPIC", "-o", str(so), str(src)], check=True)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(so))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError, match="ABI version 2"):
+        _lib.lib()
+    src.write_text("int some_other_function(void) { return 0; }\n")
+    so2 = tmp_path / "libother.so"
+    subprocess.run(["gcc", "-shared", "-fPIC", "-o", str(so2), str(src)], check=True)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(so2))
+    with pytest.raises(ImportError, match="no ep_abi_version"):
+        _lib.lib()
