@@ -43,4 +43,7 @@ from .ops import (  # noqa: F401
     ep_regroup_by_expert,
     ep_regroup_workspace_bytes,
     workspace_for,
+    ep_workspace_status,
+    check_workspaces,
+    WaitGaveUpError,
 )

@@ -446,4 +446,19 @@ hipError_t launch_batched_scan(const ScanArgs& a, hipStream_t s) {
   return launch_scan<kModeBatched>(a, s, unsigned(tiles));
 }
 
+namespace {
+// The error word of a workspace header handed to the caller and cleared in
+// one atomic exchange, so a flag set by a later call is never lost.
+__global__ void workspace_status_kernel(uint32_t* ctrl, int32_t* flags) {
+  if (threadIdx.x == 0)
+    flags[0] = int32_t(__hip_atomic_exchange(&ctrl[kCtrlError], 0u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+}  // namespace
+
+hipError_t launch_workspace_status(uint32_t* ctrl, int32_t* flags, hipStream_t s) {
+  workspace_status_kernel<<<1, kWave, 0, s>>>(ctrl, flags);
+  return hipGetLastError();
+}
+
 }  // namespace epdc

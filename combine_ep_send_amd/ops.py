@@ -14,7 +14,7 @@ from typing import NamedTuple, Optional
 import torch
 
 from ._lib import (EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3, EP_SCALE_F32, EP_SCALE_POW2, EP_SCALE_UE8M0,
-                   check, lib)
+                   EP_WS_WAIT_GAVE_UP, EpError, check, lib)
 
 __all__ = [
     "Counts",
@@ -36,6 +36,9 @@ __all__ = [
     "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes",
     "workspace_for",
+    "ep_workspace_status",
+    "check_workspaces",
+    "WaitGaveUpError",
 ]
 
 
@@ -107,7 +110,7 @@ def ep_batched_workspace_bytes(num_tokens: int, num_local_experts: int, max_num_
                                                 int(max_num_tokens)))
 
 
-_WORKSPACES = {}
+_WORKSPACES = {}      # (device index, stream handle, kind) -> (workspace, stream)
 
 
 def workspace_for(nbytes: int, device: torch.device, stream=None,
@@ -120,12 +123,62 @@ def workspace_for(nbytes: int, device: torch.device, stream=None,
     s = stream if stream is not None else torch.cuda.current_stream(device)
     key = (device.index if device.index is not None else torch.cuda.current_device(),
            s.cuda_stream, kind)
-    ws = _WORKSPACES.get(key)
+    ws = _WORKSPACES.get(key, (None, None))[0]
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:             # kept, so that check_workspaces still sees its flags
+            _RETIRED.append((key, _WORKSPACES[key]))
         with torch.cuda.stream(s):
             ws = torch.zeros(max(int(nbytes), 1 << 16), dtype=torch.uint8, device=device)
-        _WORKSPACES[key] = ws
+        _WORKSPACES[key] = (ws, s)
     return ws
+
+
+_RETIRED = []         # workspaces replaced by larger ones, not yet queried
+
+
+class WaitGaveUpError(EpError):
+    """A bounded wait inside a call (grid barrier or scan lookback) gave up:
+    the outputs of the call that waited are undefined."""
+
+
+def ep_workspace_status(workspace: torch.Tensor, *, stream=None) -> int:
+    """The error word a workspace has collected since the previous query
+    (bit EP_WS_WAIT_GAVE_UP: a bounded wait gave up), cleared by the query.
+    Enqueues the query on ``stream`` (default: the current stream) and waits
+    for that stream to reach it."""
+    _gpu(workspace, "workspace", torch.uint8)
+    s = stream if stream is not None else torch.cuda.current_stream(workspace.device)
+    with torch.cuda.stream(s):
+        flags = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+        st = lib().ep_workspace_status(_vp(workspace), workspace.numel(), _vp(flags), _stream(s))
+    check(st, "ep_workspace_status")
+    s.synchronize()
+    return int(flags.item())
+
+
+def _raise_on_flags(found):
+    bad = [(f, kind, dev) for f, kind, dev in found if f]
+    if bad:
+        what = ", ".join(f"{kind} workspace on cuda:{dev} (flags {f:#x})" for f, kind, dev in bad)
+        raise WaitGaveUpError(f"a bounded wait gave up, so the outputs of a call that used it "
+                              f"are undefined: {what}")
+
+
+def check_workspaces(*workspaces: torch.Tensor) -> None:
+    """Query the given workspaces (default: every workspace ``workspace_for``
+    has handed out, each on its own stream) and raise WaitGaveUpError if any
+    recorded a give-up since its last query.  Synchronizes those streams."""
+    found = []
+    if workspaces:
+        for ws in workspaces:
+            found.append((ep_workspace_status(ws), "given", ws.device.index))
+    else:
+        for (dev, _, kind), (ws, s) in list(_WORKSPACES.items()):
+            found.append((ep_workspace_status(ws, stream=s), kind, dev))
+        while _RETIRED:
+            (dev, _, kind), (ws, s) = _RETIRED.pop()
+            found.append((ep_workspace_status(ws, stream=s), kind, dev))
+    _raise_on_flags(found)
 
 
 # ---------------------------------------------------------------------------

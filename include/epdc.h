@@ -87,7 +87,7 @@ typedef enum {
     EP_SCALE_UE8M0 = 2         /* that power as a UE8M0 byte, 4 per int32 */
 } ep_scale_fmt_t;
 
-#define EPDC_ABI_VERSION 3
+#define EPDC_ABI_VERSION 4
 #define EPDC_MAX_TOPK 16
 #define EPDC_MAX_BINS 1024
 #define EPDC_FP8_GROUP 128
@@ -97,6 +97,37 @@ int ep_abi_version(void);
 
 /* Static, human-readable text for a status code. */
 const char* ep_status_string(int status);
+
+/* Bits of the error word that ep_workspace_status reports. */
+#define EP_WS_WAIT_GAVE_UP 1   /* a bounded wait inside a call gave up */
+
+/*
+ * Errors a workspace has collected since the last query, copied to `flags`
+ * and cleared.
+ * axolotl "torch_dispatch", module overview (hang safety): there, every
+ * rank derives its split sizes from the same routing, so that no rank waits
+ * for data that never comes.  On one GPU the only waits are between the
+ * workgroups of one launch (the grid barrier of ep_dispatch_layout and
+ * ep_regroup_by_expert, the lookback of ep_build_send_layout,
+ * ep_batched_prepare and ep_batched_prepare_fp8), and each is bounded: a
+ * wait that outlasts its limit gives up, sets EP_WS_WAIT_GAVE_UP in the
+ * workspace header (word 3) and the call carries on, so every kernel
+ * finishes but that call's outputs are undefined.  This call makes such a
+ * give-up visible to the caller.
+ *
+ *   workspace        any workspace the calls above were given (at least its
+ *                    256-byte header, 256-byte aligned)
+ *   flags            [1] int32 out, DEVICE memory: the error word (0 = no
+ *                    wait gave up) as it stood when this call's kernel ran
+ * Like the other calls it only enqueues a kernel on `stream` (run it on the
+ * stream of the calls it is meant to cover) and never synchronizes; read
+ * `flags` after the stream has finished.  The word is cleared in the same
+ * atomic step, so each query reports what happened since the previous one.
+ * Returns EP_ERR_INVALID_ARG for a null or misaligned `flags` and
+ * EP_ERR_WORKSPACE for a missing, misaligned or too small workspace.
+ */
+int ep_workspace_status(void* workspace, size_t workspace_bytes, int32_t* flags,
+                        hipStream_t stream);
 
 /*
  * Bytes of workspace ep_compute_send_counts needs: a 256-byte header (uint32
@@ -226,9 +257,10 @@ size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
  *   workspace                   ep_dispatch_layout_workspace_bytes(T, P, E_local)
  * The launch uses at most one workgroup per compute unit and one grid-wide
  * barrier; the workgroups must be able to run at the same time, which holds
- * unless other work keeps the device full for the barrier's whole time-out
- * (about 0.1 s), after which the call gives up, sets the error bit in the
- * workspace header and its outputs are undefined.  Returns
+ * unless other work keeps the device full for the barrier's whole time-out,
+ * after which the call gives up, sets EP_WS_WAIT_GAVE_UP in the workspace
+ * header (ep_workspace_status reports it) and its outputs are undefined.
+ * Returns
  * EP_ERR_UNSUPPORTED when a workgroup's LDS share (P, E and the tiles per
  * workgroup) would exceed 64 KiB; the two separate calls cover those sizes.
  */
