@@ -37,6 +37,8 @@ from .ops import (  # noqa: F401
     ep_compute_send_counts,
     ep_dispatch_layout,
     ep_dispatch_layout_workspace_bytes,
+    ep_dispatch_layout_noalloc,
+    library_scratch_status,
     ep_counts_workspace_bytes,
     ep_dispatch_permute,
     ep_layout_workspace_bytes,

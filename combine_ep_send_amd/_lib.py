@@ -16,6 +16,7 @@ EP_ERR_UNSUPPORTED = -2
 EP_ERR_WORKSPACE = -3
 EP_ERR_LAUNCH = -4
 EP_WS_WAIT_GAVE_UP = 1
+NOALLOC_SCRATCH_BYTES = 4 << 20
 EP_DTYPE_BF16 = 0
 EP_DTYPE_FP8_E4M3 = 1
 EP_SCALE_F32 = 0
@@ -42,6 +43,8 @@ _SIGNATURES = {
     "ep_dispatch_layout": (
         _I32, [_P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                _P, _SZ, _P]),
+    "ep_dispatch_layout_noalloc": (
+        _I32, [_P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_regroup_workspace_bytes": (_SZ, [_I64, _I32]),
     "ep_regroup_by_expert": (
         _I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P,
@@ -59,7 +62,7 @@ _lib = None
 
 
 # EPDC_ABI_VERSION of include/epdc.h that the signatures above follow
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 def header_functions():

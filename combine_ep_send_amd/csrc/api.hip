@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/epdc.h"
 #include "epdc_launch.h"
@@ -89,6 +90,9 @@ struct FusedShape {
   int64_t tiles, per, groups;
   bool fits;
 };
+// The library's own scratch on the current device (defined below).
+int library_scratch(void** out, hipStream_t stream);
+
 FusedShape fused_shape(int64_t T, int bins, int E) {
   FusedShape f{};
   f.waves = fused_waves(T);
@@ -122,8 +126,12 @@ const char* ep_status_string(int status) {
 int ep_workspace_status(void* workspace, size_t workspace_bytes, int32_t* flags,
                         hipStream_t stream) {
   if (!flags || !aligned(flags, 4)) return EP_ERR_INVALID_ARG;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kWsHeaderBytes)
+  if (!workspace) {                       // the library's own scratch on this device
+    const int st = library_scratch(&workspace, stream);
+    if (st != EP_OK) return st;
+  } else if (!aligned(workspace, 256) || workspace_bytes < kWsHeaderBytes) {
     return EP_ERR_WORKSPACE;
+  }
   return launch_status(launch_workspace_status(static_cast<uint32_t*>(workspace), flags, stream));
 }
 
@@ -234,13 +242,54 @@ size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
   return fused_ws_bytes(num_tokens, num_ranks, nh);
 }
 
-int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64_t num_tokens,
-                       int num_topk, int num_ranks, int num_local_experts,
-                       int64_t num_send_capacity, int32_t* dest, uint8_t* is_in_rank,
-                       int32_t* send_counts, int32_t* tokens_per_expert, int32_t* diag,
-                       int32_t* send_token_idx, int32_t* send_rank, int32_t* send_idx,
-                       float* send_w, int32_t* token_row, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The scratch of ep_dispatch_layout_noalloc: one copy on every GPU the
+// library runs on, held until the process ends.  Host code never uses this
+// name as an address (it is a host-side stand-in): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[EPDC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch.  The first call on a
+// device looks it up and clears the control header on `stream` (a kernel,
+// not a memset, so that it can sit in a captured graph); later calls find
+// the header as the previous call left it, ready for the next.
+int library_scratch(void** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EP_ERR_LAUNCH;
+  ScratchSlot& slot = g_scratch[dev];
+  bool first = false;
+  std::call_once(slot.once, [&] {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+    first = true;
+  });
+  if (slot.err != hipSuccess || slot.ptr == nullptr) return EP_ERR_LAUNCH;
+  if (first && launch_clear_header(static_cast<uint32_t*>(slot.ptr), stream) != hipSuccess)
+    return EP_ERR_LAUNCH;
+  *out = slot.ptr;
+  return EP_OK;
+}
+
+// ep_dispatch_layout, with the workspace given or (workspace == nullptr and
+// use_scratch) the library's own scratch; every argument is validated
+// before anything is enqueued.
+int dispatch_layout_impl(const int64_t* topk_idx, const float* topk_weights, int64_t num_tokens,
+                         int num_topk, int num_ranks, int num_local_experts,
+                         int64_t num_send_capacity, int32_t* dest, uint8_t* is_in_rank,
+                         int32_t* send_counts, int32_t* tokens_per_expert, int32_t* diag,
+                         int32_t* send_token_idx, int32_t* send_rank, int32_t* send_idx,
+                         float* send_w, int32_t* token_row, void* workspace,
+                         size_t workspace_bytes, bool use_scratch, hipStream_t stream) {
   int st = check_routing(num_tokens, num_topk, num_ranks, num_local_experts);
   if (st != EP_OK) return st;
   if (num_ranks > EPDC_MAX_BINS) return EP_ERR_UNSUPPORTED;
@@ -255,13 +304,19 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
       !arr_ok(send_rank, cap, 4) || !arr_ok(send_idx, cap, 4) || !arr_ok(send_w, cap, 4) ||
       (tokens_per_expert && !aligned(tokens_per_expert, 4)) || (diag && !aligned(diag, 4)))
     return EP_ERR_INVALID_ARG;
-  if (!workspace || !aligned(workspace, 256) ||
-      workspace_bytes < ep_dispatch_layout_workspace_bytes(num_tokens, num_ranks,
-                                                           num_local_experts))
+  const size_t need = ep_dispatch_layout_workspace_bytes(num_tokens, num_ranks, num_local_experts);
+  if (use_scratch) {
+    if (need > EPDC_NOALLOC_SCRATCH_BYTES) return EP_ERR_WORKSPACE;
+  } else if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) {
     return EP_ERR_WORKSPACE;
+  }
   const int E = num_ranks * num_local_experts;
   const FusedShape sh = fused_shape(num_tokens, num_ranks, E);
   if (!sh.fits) return EP_ERR_UNSUPPORTED;
+  if (use_scratch) {
+    st = library_scratch(&workspace, stream);
+    if (st != EP_OK) return st;
+  }
 
   FusedArgs a{};
   a.topk_idx = topk_idx;
@@ -292,6 +347,36 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64
   a.waves = sh.waves;
   set_fused_workspace(a, workspace, num_ranks, int64_t(num_ranks) + E + 1, sh.groups);
   return launch_status(launch_dispatch_layout(a, unsigned(sh.groups), stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights, int64_t num_tokens,
+                       int num_topk, int num_ranks, int num_local_experts,
+                       int64_t num_send_capacity, int32_t* dest, uint8_t* is_in_rank,
+                       int32_t* send_counts, int32_t* tokens_per_expert, int32_t* diag,
+                       int32_t* send_token_idx, int32_t* send_rank, int32_t* send_idx,
+                       float* send_w, int32_t* token_row, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return dispatch_layout_impl(topk_idx, topk_weights, num_tokens, num_topk, num_ranks,
+                              num_local_experts, num_send_capacity, dest, is_in_rank, send_counts,
+                              tokens_per_expert, diag, send_token_idx, send_rank, send_idx, send_w,
+                              token_row, workspace, workspace_bytes, false, stream);
+}
+
+int ep_dispatch_layout_noalloc(const int64_t* topk_idx, const float* topk_weights,
+                               int64_t num_tokens, int num_topk, int num_ranks,
+                               int num_local_experts, int64_t num_send_capacity, int32_t* dest,
+                               uint8_t* is_in_rank, int32_t* send_counts,
+                               int32_t* tokens_per_expert, int32_t* diag,
+                               int32_t* send_token_idx, int32_t* send_rank, int32_t* send_idx,
+                               float* send_w, int32_t* token_row, hipStream_t stream) {
+  return dispatch_layout_impl(topk_idx, topk_weights, num_tokens, num_topk, num_ranks,
+                              num_local_experts, num_send_capacity, dest, is_in_rank, send_counts,
+                              tokens_per_expert, diag, send_token_idx, send_rank, send_idx, send_w,
+                              token_row, nullptr, 0, true, stream);
 }
 
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins) {

@@ -16,6 +16,8 @@ enum : int { kCtrlTicket = 0, kCtrlDone = 1, kCtrlEpoch = 2, kCtrlError = 3 };
 constexpr uint32_t kErrLookbackGaveUp = 1u;   // a bounded wait (lookback or barrier) gave up
 // Copy a workspace's error word [kCtrlError] to flags[0] and clear it.
 hipError_t launch_workspace_status(uint32_t* ctrl, int32_t* flags, hipStream_t s);
+// Zero a workspace's 256-byte control header.
+hipError_t launch_clear_header(uint32_t* ctrl, hipStream_t s);
 
 // The layout scans work on tiles of 256 tokens (one workgroup each).
 inline int64_t num_tiles(int64_t T) { return (T + 255) / 256; }

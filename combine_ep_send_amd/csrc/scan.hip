@@ -454,10 +454,20 @@ __global__ void workspace_status_kernel(uint32_t* ctrl, int32_t* flags) {
     flags[0] = int32_t(__hip_atomic_exchange(&ctrl[kCtrlError], 0u, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT));
 }
+
+// Zero the 256-byte control header of a workspace (one word per thread).
+__global__ void clear_header_kernel(uint32_t* ctrl) {
+  if (threadIdx.x < kWsHeaderBytes / 4) ctrl[threadIdx.x] = 0u;
+}
 }  // namespace
 
 hipError_t launch_workspace_status(uint32_t* ctrl, int32_t* flags, hipStream_t s) {
   workspace_status_kernel<<<1, kWave, 0, s>>>(ctrl, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_header(uint32_t* ctrl, hipStream_t s) {
+  clear_header_kernel<<<1, kWsHeaderBytes / 4, 0, s>>>(ctrl);
   return hipGetLastError();
 }
 

@@ -23,6 +23,8 @@ __all__ = [
     "ep_build_send_layout",
     "ep_dispatch_layout",
     "ep_dispatch_layout_workspace_bytes",
+    "ep_dispatch_layout_noalloc",
+    "library_scratch_status",
     "ep_dispatch_permute",
     "ep_regroup_by_expert",
     "ep_regroup_workspace_bytes",
@@ -330,6 +332,58 @@ def ep_dispatch_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor, num_r
         _stream(stream))
     check(st, "ep_dispatch_layout")
     return counts, out
+
+
+def ep_dispatch_layout_noalloc(topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+                               num_ranks: int, num_local_experts: int, num_send_capacity: int,
+                               *, counts: Counts, out: SendLayout, stream=None):
+    """ep_dispatch_layout on the library's own scratch (no workspace, no
+    allocation): the caller passes every output (``counts`` with C = 1 and
+    ``out``), as ep_dispatch_layout takes them."""
+    _gpu(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    P, El, cap = int(num_ranks), int(num_local_experts), int(num_send_capacity)
+    E = P * El
+    _shape(_gpu(topk_weights, "topk_weights", torch.float32), "topk_weights", (T, K))
+    _shape(_gpu(counts.dest, "dest", torch.int32), "dest", (T, K))
+    _shape(_gpu(counts.is_in_rank, "is_in_rank", torch.uint8), "is_in_rank", (T, P))
+    _gpu(counts.send_counts, "send_counts", torch.int32)
+    if counts.send_counts.numel() != P:
+        raise ValueError("send_counts must hold P counts (one chunk)")
+    if counts.tokens_per_expert is not None:
+        _gpu(counts.tokens_per_expert, "tokens_per_expert", torch.int32)
+        if counts.tokens_per_expert.numel() != E:
+            raise ValueError("tokens_per_expert must hold E counts")
+    _shape(_gpu(counts.diag, "diag", torch.int32), "diag", (1,))
+    for name, t, dt in (("send_token_idx", out.send_token_idx, torch.int32),
+                        ("send_rank", out.send_rank, torch.int32),
+                        ("send_idx", out.send_idx, torch.int32),
+                        ("send_w", out.send_w, torch.float32)):
+        _gpu(t, name, dt)
+        if t.shape[0] < cap:
+            raise ValueError(f"{name} holds fewer than {cap} rows")
+    if out.send_idx.dim() != 2 or out.send_idx.shape[1] != K or out.send_w.shape[1:] != (K,):
+        raise ValueError("send_idx / send_w must be [cap, K]")
+    _shape(_gpu(out.token_row, "token_row", torch.int32), "token_row", (T, K))
+    st = lib().ep_dispatch_layout_noalloc(
+        _vp(topk_idx), _vp(topk_weights), T, K, P, El, cap, _vp(counts.dest),
+        _vp(counts.is_in_rank), _vp(counts.send_counts), _vp(counts.tokens_per_expert),
+        _vp(counts.diag), _vp(out.send_token_idx), _vp(out.send_rank), _vp(out.send_idx),
+        _vp(out.send_w), _vp(out.token_row), _stream(stream))
+    check(st, "ep_dispatch_layout_noalloc")
+    return counts, out
+
+
+def library_scratch_status(*, stream=None) -> int:
+    """ep_workspace_status of the library's own scratch on the current device
+    (the one ep_dispatch_layout_noalloc uses), read back after ``stream``."""
+    s = stream if stream is not None else torch.cuda.current_stream()
+    with torch.cuda.stream(s):
+        flags = torch.zeros(1, dtype=torch.int32, device=torch.device("cuda", s.device.index))
+        st = lib().ep_workspace_status(None, 0, _vp(flags), _stream(s))
+    check(st, "ep_workspace_status")
+    s.synchronize()
+    return int(flags.item())
 
 
 def ep_regroup_workspace_bytes(num_rows: int, num_bins: int) -> int:

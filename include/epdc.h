@@ -87,10 +87,12 @@ typedef enum {
     EP_SCALE_UE8M0 = 2         /* that power as a UE8M0 byte, 4 per int32 */
 } ep_scale_fmt_t;
 
-#define EPDC_ABI_VERSION 4
+#define EPDC_ABI_VERSION 5
 #define EPDC_MAX_TOPK 16
 #define EPDC_MAX_BINS 1024
 #define EPDC_FP8_GROUP 128
+/* Bytes of the library's own scratch per GPU (ep_dispatch_layout_noalloc). */
+#define EPDC_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Version of this ABI (EPDC_ABI_VERSION). */
 int ep_abi_version(void);
@@ -116,7 +118,9 @@ const char* ep_status_string(int status);
  * give-up visible to the caller.
  *
  *   workspace        any workspace the calls above were given (at least its
- *                    256-byte header, 256-byte aligned)
+ *                    256-byte header, 256-byte aligned), or NULL for the
+ *                    library's own scratch on the current device (the one
+ *                    ep_dispatch_layout_noalloc uses)
  *   flags            [1] int32 out, DEVICE memory: the error word (0 = no
  *                    wait gave up) as it stood when this call's kernel ran
  * Like the other calls it only enqueues a kernel on `stream` (run it on the
@@ -273,6 +277,30 @@ int ep_dispatch_layout(const int64_t* topk_idx, const float* topk_weights,
                        int32_t* send_idx, float* send_w, int32_t* token_row,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/*
+ * ep_dispatch_layout for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same outputs
+ * bit for bit.  Its workspace is the library's own scratch, a static device
+ * array of EPDC_NOALLOC_SCRATCH_BYTES on each GPU, held until the process
+ * ends; the first call on a GPU looks up its address and clears its control
+ * header (one small kernel on `stream`).  No call allocates or frees memory.
+ * Calls whose workspace would need more (ep_dispatch_layout_workspace_bytes
+ * above the limit; at P = 32 and E = 256 the need is about 82 KiB) return
+ * EP_ERR_WORKSPACE.  Every call on one GPU shares that GPU's scratch, so
+ * calls that may overlap in time on one GPU (other streams, other host
+ * threads) race and must not be made; ep_workspace_status(NULL, ...)
+ * reports its error word.
+ */
+int ep_dispatch_layout_noalloc(const int64_t* topk_idx, const float* topk_weights,
+                               int64_t num_tokens, int num_topk, int num_ranks,
+                               int num_local_experts, int64_t num_send_capacity,
+                               int32_t* dest, uint8_t* is_in_rank, int32_t* send_counts,
+                               int32_t* tokens_per_expert, int32_t* diag,
+                               int32_t* send_token_idx, int32_t* send_rank,
+                               int32_t* send_idx, float* send_w, int32_t* token_row,
+                               hipStream_t stream);
 
 /*
  * Bytes of workspace ep_regroup_by_expert needs for R received rows and

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 EXPECTED = {
     "ep_abi_version", "ep_status_string", "ep_workspace_status", "ep_counts_workspace_bytes", "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
-    "ep_dispatch_layout_workspace_bytes", "ep_dispatch_layout",
+    "ep_dispatch_layout_workspace_bytes", "ep_dispatch_layout", "ep_dispatch_layout_noalloc",
     "ep_regroup_workspace_bytes", "ep_regroup_by_expert",
     "ep_dispatch_permute", "ep_batched_prepare", "ep_batched_prepare_fp8", "ep_combine",
 }
@@ -43,9 +43,9 @@ def test_bindings_follow_the_header_version():
 
 
 def test_version_and_status_strings():
-    # version 4: ep_workspace_status
+    # version 5: ep_dispatch_layout_noalloc (version 4: ep_workspace_status)
     L = _lib.lib()
-    assert L.ep_abi_version() == 4
+    assert L.ep_abi_version() == 5
     assert L.ep_status_string(0) == b"ok"
     for s in (-1, -2, -3, -4):
         assert L.ep_status_string(s) not in (b"ok", b"unknown status")
@@ -155,6 +155,30 @@ def test_fused_layout_workspace_and_arguments():
     assert call(ws_bytes=64) == _lib.EP_ERR_WORKSPACE
     # LDS share over 64 KiB (1024 destinations x 8 experts): use the two calls
     assert call(T=20000, P=1024, El=8) == _lib.EP_ERR_UNSUPPORTED
+
+
+def test_noalloc_layout_rejects_before_touching_the_gpu():
+    L = _lib.lib()
+    f = L.ep_dispatch_layout_noalloc
+
+    def call(T=16, K=2, P=2, El=4, cap=64, dest=A16, tpe=None):
+        return f(A16, A16, T, K, P, El, cap, dest, A16, A16, tpe, None, A16, A16, A16, A16,
+                 A16, None)
+    assert call(T=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(K=17) == _lib.EP_ERR_UNSUPPORTED
+    assert call(cap=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(dest=ODD) == _lib.EP_ERR_INVALID_ARG
+    # a workspace need past the scratch: 256 workgroups x (1024 + 8192 + 1 + 1024) words
+    need = L.ep_dispatch_layout_workspace_bytes(1 << 20, 1024, 8)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(T=1 << 20, P=1024, El=8, cap=1 << 20) == _lib.EP_ERR_WORKSPACE
+    # the headline shape fits with room to spare
+    assert L.ep_dispatch_layout_workspace_bytes(16384, 32, 8) < _lib.NOALLOC_SCRATCH_BYTES // 32
+    st = L.ep_workspace_status
+    assert st(A16, 1 << 20, None, None) == _lib.EP_ERR_INVALID_ARG
+    assert st(A16, 1 << 20, ODD, None) == _lib.EP_ERR_INVALID_ARG
+    assert st(A8, 1 << 20, A16, None) == _lib.EP_ERR_WORKSPACE
+    assert st(A16, 128, A16, None) == _lib.EP_ERR_WORKSPACE
 
 
 def test_regroup_workspace_and_arguments():
