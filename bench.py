@@ -149,7 +149,8 @@ def build_send_step(torch, ep, s, d_idx, d_w, d_x):
         "permute": bytes_permute(H, U, N),
         "combine": bytes_combine(H, T, K, N),
     }
-    info = {"num_send": N, "routed_tokens": U, "capacity": cap}
+    info = {"num_send": N, "routed_tokens": U, "capacity": cap,
+            "send_counts": counts.send_counts[0].tolist()}
     return step, kb, info
 
 
@@ -226,7 +227,8 @@ def build_expert_major_step(torch, ep, s, d_idx, d_w, d_x):
         "combine": 2 * H * N + 4 * T * K + 2 * H * T,
     }
     info = {"num_send": N, "routed_tokens": U, "capacity": cap, "regrouped_rows": M,
-            "regrouped_data_rows": M_data, "align": A}
+            "regrouped_data_rows": M_data, "align": A,
+            "send_counts": counts.send_counts[0].tolist()}
     return step, kb, info
 
 
@@ -261,7 +263,8 @@ def build_batched_step(torch, ep, s, d_idx, d_w, d_x):
         "batched_prepare": bytes_batched(H, T, K, El, M, U_local),
         "combine": bytes_combine(H, T, K, rows),
     }
-    return step, kb, {"rows": rows, "local_tokens": U_local}
+    return step, kb, {"rows": rows, "local_tokens": U_local,
+                      "tokens_per_expert": tpe.tolist()}
 
 
 def dequantize_batched(torch, q, sc, scale_fmt):
@@ -317,96 +320,45 @@ def build_batched_fp8_step(torch, ep, s, d_idx, d_w, d_x):
         "combine": bytes_combine(H, T, K, rows),
     }
     return step, kb, {"rows": rows, "local_tokens": U_local, "scale_fmt": fmt,
-                      "scale_col_major": colm}
+                      "scale_col_major": colm, "tokens_per_expert": tpe.tolist()}
 
 
 def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
+    """The chunked fp8 workload through the library's ChunkedDispatcher, the
+    same object the parity tests run: one count pass, per-chunk send layouts
+    with the worst-case capacity (no host sync), then per chunk on alternating
+    streams the fp8 quantize-permute and the combine.  The identity expert
+    behind fp8 returns y = bf16(decode(q) * scale), built once before timing."""
     T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, s.chunks
-    dev = d_x.device
-    bounds = ep.chunk_bounds(T, C)
-    streams = [torch.cuda.Stream(device=dev) for _ in range(s.streams)]
-    # Chunk i's permute and combine run on stream i mod S.  The layouts are
-    # latency-bound: chunk 0's runs first on stream 0, the later chunks' run
-    # back to back on stream 1 while chunk 0's permute streams rows.
-    work_st = [streams[i % len(streams)] for i in range(C)]
-    lay_st = [streams[0] if i == 0 or len(streams) == 1 else streams[1] for i in range(C)]
-    counts = ep.ep_compute_send_counts(d_idx, P, El, C, expert_counts=False)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    disp = ep.ChunkedDispatcher(T, K, H, num_local_experts=El, num_ranks=P, chunks=C, fp8=True,
+                                streams=s.streams, exact_counts=False, device=d_x.device)
+    ys = [None] * C
+
+    def dequantize(i, recv, idx, w):
+        q, sc = recv
+        n = q.shape[0]
+        ys[i] = (q.float().view(n, H // 128, 128) * sc[:, :, None]).view(n, H).to(torch.bfloat16)
+        return ys[i]
+
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=d_x.device)
+    disp.forward(d_x, d_idx, d_w, dequantize, out=out)
     torch.cuda.synchronize()
-    per = []
-    for i, (a, b) in enumerate(bounds):
-        st = lay_st[i]
-        cap = (b - a) * min(K, P)
-        ws = ep.workspace_for(ep.ep_layout_workspace_bytes(b - a, P), dev, st)
-        with torch.cuda.stream(st):
-            lay = ep.ep_build_send_layout(d_idx[a:b], d_w[a:b], counts.dest[a:b],
-                                          counts.send_counts[i], P, El, cap, stream=st,
-                                          workspace=ws)
-            q, sc = ep.ep_dispatch_permute(d_x[a:b], lay.token_row, cap, fp8=True, stream=st)
-        per.append(dict(a=a, b=b, cap=cap, lay=lay, q=q, sc=sc, ws=ws))
-    torch.cuda.synchronize()
-    # identity expert behind fp8: y = bf16(decode(q) * scale), built once
-    for c in per:
-        deq = c["q"].float().view(c["cap"], H // 128, 128) * c["sc"][:, :, None]
-        c["y"] = deq.view(c["cap"], H).to(torch.bfloat16)
-    torch.cuda.synchronize()
-    main = torch.cuda.current_stream()
+
+    def identity_expert(i, recv, idx, w):
+        return ys[i]
 
     def step(timer=None):
         # The per-kernel timing pass runs every chunk on one stream, so each
         # launch's duration is its own and not shared with the other stream's.
-        lst = lay_st if timer is None else [streams[0]] * C
-        wst = work_st if timer is None else [streams[0]] * C
-        s0 = streams[0]
-        start = torch.cuda.Event()
-        start.record(main)
-        s0.wait_event(start)
-        tk = timer.start("counts", s0) if timer else None
-        ep.ep_compute_send_counts(d_idx, P, El, C, expert_counts=False, out=counts, stream=s0)
-        if timer:
-            timer.stop(tk)
-        ready = torch.cuda.Event()
-        ready.record(s0)
-        for st in streams[1:]:
-            st.wait_event(ready)
-        laid = []
-        for i, c in enumerate(per):
-            st = lst[i]
-            a, b = c["a"], c["b"]
-            tk = timer.start("layout", st) if timer else None
-            ep.ep_build_send_layout(d_idx[a:b], d_w[a:b], counts.dest[a:b],
-                                    counts.send_counts[i], P, El, c["cap"], out=c["lay"],
-                                    workspace=c["ws"], stream=st)
-            if timer:
-                timer.stop(tk)
-            ev = torch.cuda.Event()
-            ev.record(st)
-            laid.append(ev)
-        for i, c in enumerate(per):
-            st = wst[i]
-            if st is not lst[i]:
-                st.wait_event(laid[i])
-            a, b = c["a"], c["b"]
-            tk = timer.start("permute_fp8", st) if timer else None
-            ep.ep_dispatch_permute(d_x[a:b], c["lay"].token_row, c["cap"], fp8=True, out=c["q"],
-                                   out_scale=c["sc"], stream=st)
-            if timer:
-                timer.stop(tk)
-                tk = timer.start("combine", st)
-            ep.ep_combine(c["y"], c["lay"].token_row, d_w[a:b], out=out[a:b], stream=st)
-            if timer:
-                timer.stop(tk)
-        for st in streams:
-            done = torch.cuda.Event()
-            done.record(st)
-            main.wait_event(done)
+        disp.forward(d_x, d_idx, d_w, identity_expert, out=out, timer=timer,
+                     serialize=timer is not None)
 
     step()
     torch.cuda.synchronize()
-    sc_host = counts.send_counts.cpu().numpy()
+    sc_host = disp.counts.send_counts.cpu().numpy()
     kb = {"counts": bytes_counts(T, K, P, s.E, C), "layout": 0, "permute_fp8": 0, "combine": 0}
     Ns = []
-    for i, (a, b) in enumerate(bounds):
+    for i, (a, b) in enumerate(disp.bounds):
         N = int(sc_host[i].sum())
         U = int(((d_idx[a:b] >= 0).any(dim=1)).sum().item())
         Ns.append(N)
@@ -416,6 +368,7 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     # per-launch bytes of the chunked kernels: averages over the C launches
     per_launch = {k: (v / C if k != "counts" else v) for k, v in kb.items()}
     return step, kb, {"num_send_per_chunk": Ns, "per_launch_bytes": per_launch,
+                      "send_counts": sc_host.sum(axis=0).tolist(),
                       "kernel_timing": "chunks serialized on one stream in the per-kernel pass"}
 
 
@@ -540,6 +493,20 @@ def traffic_from_profiles(workload, kernel_name, source_digest):
     return rec
 
 
+def row_skew(info):
+    """Rows per destination (send layouts) or per local expert (batched):
+    smallest, largest, mean and largest / mean."""
+    rows = info.get("send_counts", info.get("tokens_per_expert"))
+    if not rows:
+        return {}
+    r = np.asarray(rows, dtype=np.float64)
+    what = "destination" if "send_counts" in info else "local_expert"
+    return {f"rows_per_{what}": {"min": int(r.min()), "max": int(r.max()),
+                                 "mean": round(float(r.mean()), 2),
+                                 "max_over_mean": round(float(r.max() / r.mean()), 3)
+                                 if r.mean() > 0 else None}}
+
+
 class CacheClear:
     """Reads 512 MiB of device memory (a max over 128 Mi floats), which
     evicts everything the 256 MB Infinity Cache held and leaves it clean;
@@ -648,7 +615,6 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
-    w0 = time.perf_counter()
     if scratch is None:
         # Timed region: K whole steps between two events on the main stream
         # (the chunked workload joins its side streams back into it every step).
@@ -683,9 +649,7 @@ def main():
         step_ms = [a.elapsed_time(c) - clear_ms for a, _, c in evs]
         events_ms = [a.elapsed_time(b) for a, b, _ in evs]
         ms = float(np.mean(step_ms))
-    wall = time.perf_counter() - w0
-    log(f"[bench] {args.steps} timed steps: {ms:.4f} ms/step (events), "
-        f"{1000 * wall / args.steps:.4f} ms/step (wall)")
+    log(f"[bench] {args.steps} timed steps: {ms:.4f} ms/step (events)")
 
     # Per-kernel durations: the same K steps again, each kernel bracketed by
     # HIP events on the stream it is launched on.  (Events between kernels
@@ -697,6 +661,12 @@ def main():
         step(timer)
     torch.cuda.synchronize()
     kern_us = timer.averages_us()
+    # every bounded wait of the steps above must have ended normally: a wait
+    # that gave up leaves its flag in the workspace, and that step's outputs
+    # would be undefined
+    ws_errors = sum(1 for f, _, _ in ep.workspace_flags() if f)
+    if ws_errors:
+        log(f"[bench] {ws_errors} workspace(s) report a bounded wait that gave up")
     per_launch = info.get("per_launch_bytes", kbytes)
     dom = max((k for k in kern_us if k not in ("counts", "layout", "dispatch_layout",
                                                    "regroup")),
@@ -727,11 +697,11 @@ def main():
             "streams": s.streams, "seed": s.seed, "parallelism": "single GPU",
             "mall_flush_between_steps": not args.back_to_back,
             **{k: v for k, v in info.items() if k != "per_launch_bytes"},
+            **row_skew(info),
         },
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "alg_bytes_per_step": total_bytes,
-        "wall_ms_per_step": round(1000 * wall / args.steps, 5),
         "step_timing": ("one event pair around K back-to-back steps" if args.back_to_back else
                         "each step starts on a cache cleared by a 512 MiB read; its time "
                         "runs to the end of the next clearing read (which writes back the "
@@ -740,6 +710,7 @@ def main():
             "clean_clear_ms": round(clear_ms, 5),
             "ms_per_step_to_last_kernel": round(float(np.mean(events_ms)), 5)}),
         "kernel_avg_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "workspace_errors": ws_errors,
         "roofline": {
             "kernel": dom,
             "bound": "hbm",

@@ -11,6 +11,7 @@ fails loudly if ``libepdc.so`` has not been built.
 
 from ._lib import LIB_PATH, header_functions, lib  # noqa: F401
 from .dispatch import (  # noqa: F401
+    ChunkedDispatcher,
     DispatchHandle,
     batched_finalize,
     batched_prepare,
@@ -47,5 +48,6 @@ from .ops import (  # noqa: F401
     workspace_for,
     ep_workspace_status,
     check_workspaces,
+    workspace_flags,
     WaitGaveUpError,
 )

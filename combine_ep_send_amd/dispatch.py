@@ -12,10 +12,10 @@ from typing import Callable, List, NamedTuple, Optional, Tuple
 
 import torch
 
-from .ops import (Regrouped, ep_batched_prepare, ep_batched_prepare_fp8, ep_build_send_layout,
-                  ep_combine,
-                  ep_compute_send_counts, ep_dispatch_layout, ep_dispatch_permute,
-                  ep_regroup_by_expert)
+from .ops import (Counts, Regrouped, SendLayout, ep_batched_prepare, ep_batched_prepare_fp8,
+                  ep_build_send_layout, ep_combine, ep_compute_send_counts,
+                  ep_counts_workspace_bytes, ep_dispatch_layout, ep_dispatch_permute,
+                  ep_layout_workspace_bytes, ep_regroup_by_expert, workspace_for)
 
 __all__ = [
     "chunk_bounds",
@@ -26,6 +26,7 @@ __all__ = [
     "dispatch",
     "combine",
     "dispatch_chunked_forward",
+    "ChunkedDispatcher",
     "batched_prepare",
     "batched_finalize",
     "permute_by_expert",
@@ -130,72 +131,180 @@ def combine(local_out: torch.Tensor, handle: DispatchHandle,
                       bias=bias, out=out)
 
 
+class ChunkedDispatcher:
+    """dispatch -> local kernel -> combine over contiguous token chunks,
+    alternating over HIP streams (axolotl "torch_dispatch":
+    dispatch_chunked_forward, chunk_bounds).
+
+    Everything a forward touches is allocated once, for one shape (T, K, H,
+    P, E_local, chunks): the counts, each chunk's send layout and send
+    buffer (bf16, or fp8 codes + per-128-channel scales), the workspaces and
+    the streams, so repeated forwards allocate nothing but events.
+
+    One forward, in enqueue order:
+      1. stream 0 waits for the caller's stream and counts every chunk in one
+         pass ([C, P] send counts);
+      2. with ``exact_counts`` the counts reach the host in ONE copy and size
+         each chunk exactly; otherwise each chunk gets its worst case
+         T_c * min(K, P) rows and nothing waits on the host;
+      3. the send layouts: chunk 0's on stream 0, the later chunks' back to
+         back on stream 1 (they are latency-bound, and run while chunk 0's
+         rows stream);
+      4. chunk c on stream c mod S: the row permute, ``local_kernel(c,
+         recv_x, recv_idx, recv_w)`` (bf16 expert output [rows, H], enqueued
+         on that stream), then the weighted combine into out[start:end];
+      5. the caller's stream waits for every stream.
+    Chunk c+1's permute is enqueued before chunk c's combine is consumed.
+    ``timer`` (start(name, stream) / stop(token)) brackets every launch with
+    events; ``serialize`` puts all of it on stream 0."""
+
+    def __init__(self, num_tokens: int, num_topk: int, hidden: int, *, num_local_experts: int,
+                 num_ranks: int, chunks: int, fp8: bool = False, streams=2,
+                 exact_counts: bool = False, device=None):
+        self.T, self.K, self.H = int(num_tokens), int(num_topk), int(hidden)
+        self.P, self.El, self.C = int(num_ranks), int(num_local_experts), int(chunks)
+        self.fp8, self.exact_counts = bool(fp8), bool(exact_counts)
+        dev = torch.device(device) if device is not None else torch.device(
+            "cuda", torch.cuda.current_device())
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        if isinstance(streams, int):
+            streams = [torch.cuda.Stream(device=dev) for _ in range(streams)]
+        if not streams:
+            raise ValueError("at least one stream")
+        self.streams = list(streams)
+        self.bounds = chunk_bounds(self.T, self.C)
+        self.worst = [(e - s) * min(self.K, self.P) for s, e in self.bounds]
+        self.caps = list(self.worst)
+        T, K, P, H = self.T, self.K, self.P, self.H
+        s0 = self.streams[0]
+        self.counts = Counts(
+            dest=torch.empty((T, K), dtype=torch.int32, device=dev),
+            is_in_rank=torch.empty((T, P), dtype=torch.uint8, device=dev),
+            send_counts=torch.empty((self.C, P), dtype=torch.int32, device=dev),
+            tokens_per_expert=None,
+            diag=torch.empty(1, dtype=torch.int32, device=dev))
+        self.ws_counts = workspace_for(ep_counts_workspace_bytes(T, P, self.El, self.C), dev, s0,
+                                       "counts")
+        self.layouts, self.recv, self.ws_layout = [], [], []
+        for i, cap in enumerate(self.worst):
+            self.layouts.append(SendLayout(
+                send_token_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+                send_rank=torch.empty(cap, dtype=torch.int32, device=dev),
+                send_idx=torch.empty((cap, K), dtype=torch.int32, device=dev),
+                send_w=torch.empty((cap, K), dtype=torch.float32, device=dev),
+                token_row=torch.empty((self.bounds[i][1] - self.bounds[i][0], K),
+                                      dtype=torch.int32, device=dev)))
+            if self.fp8:
+                self.recv.append((torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev),
+                                  torch.empty((cap, H // 128), dtype=torch.float32, device=dev)))
+            else:
+                self.recv.append(torch.empty((cap, H), dtype=torch.bfloat16, device=dev))
+            n = self.bounds[i][1] - self.bounds[i][0]
+            st = self._layout_stream(i, False)
+            self.ws_layout.append(workspace_for(ep_layout_workspace_bytes(max(n, 1), P), dev, st))
+
+    def _layout_stream(self, i: int, serialize: bool):
+        if serialize or i == 0 or len(self.streams) == 1:
+            return self.streams[0]
+        return self.streams[1]
+
+    def forward(self, x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+                local_kernel: Callable, *, out: Optional[torch.Tensor] = None, timer=None,
+                serialize: bool = False) -> torch.Tensor:
+        T, K, P, El, H = self.T, self.K, self.P, self.El, self.H
+        if tuple(x.shape) != (T, H) or tuple(topk_idx.shape) != (T, K) or \
+                tuple(topk_weights.shape) != (T, K):
+            raise ValueError(f"inputs must be x [{T}, {H}], topk_idx / topk_weights [{T}, {K}]")
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=self.device)
+        main = torch.cuda.current_stream(self.device)
+        streams = self.streams[:1] if serialize else self.streams
+        s0 = streams[0]
+
+        def mark(name, st):
+            return timer.start(name, st) if timer is not None else None
+
+        def done(tok):
+            if tok is not None:
+                timer.stop(tok)
+
+        start = torch.cuda.Event()
+        start.record(main)
+        s0.wait_event(start)
+        tk = mark("counts", s0)
+        ep_compute_send_counts(topk_idx, P, El, self.C, expert_counts=False, out=self.counts,
+                               workspace=self.ws_counts, stream=s0)
+        done(tk)
+        if self.exact_counts:
+            with torch.cuda.stream(s0):
+                self.caps = [int(v) for v in to_host(self.counts.send_counts).sum(dim=1)]
+        ready = torch.cuda.Event()
+        ready.record(s0)
+        for st in streams[1:]:
+            st.wait_event(ready)
+        laid = []
+        for i, (a, b) in enumerate(self.bounds):
+            st = self._layout_stream(i, serialize)
+            if b > a:
+                tk = mark("layout", st)
+                ep_build_send_layout(topk_idx[a:b], topk_weights[a:b], self.counts.dest[a:b],
+                                     self.counts.send_counts[i], P, El, self.caps[i],
+                                     out=self.layouts[i], workspace=self.ws_layout[i], stream=st)
+                done(tk)
+            ev = torch.cuda.Event()
+            ev.record(st)
+            laid.append((ev, st))
+        for i, (a, b) in enumerate(self.bounds):
+            if b == a:
+                continue
+            st = streams[i % len(streams)]
+            ev, lst = laid[i]
+            if lst is not st:
+                st.wait_event(ev)
+            lay = self.layouts[i]
+            tk = mark("permute_fp8" if self.fp8 else "permute", st)
+            if self.fp8:
+                q, sc = self.recv[i]
+                ep_dispatch_permute(x[a:b], lay.token_row, self.caps[i], fp8=True, out=q,
+                                    out_scale=sc, stream=st)
+                recv_x = (q, sc)
+            else:
+                recv_x = ep_dispatch_permute(x[a:b], lay.token_row, self.caps[i],
+                                             out=self.recv[i], stream=st)
+            done(tk)
+            with torch.cuda.stream(st):
+                y = local_kernel(i, recv_x, lay.send_idx, lay.send_w)
+            tk = mark("combine", st)
+            ep_combine(y, lay.token_row, topk_weights[a:b], out=out[a:b], stream=st)
+            done(tk)
+        for st in streams:
+            fin = torch.cuda.Event()
+            fin.record(st)
+            main.wait_event(fin)
+        return out
+
+
 def dispatch_chunked_forward(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
                              local_kernel: Callable, *, num_local_experts: int, num_ranks: int,
-                             chunks: int, fp8: bool = False, streams: Optional[list] = None,
+                             chunks: int, fp8: bool = False, streams=None,
                              exact_counts: bool = True) -> torch.Tensor:
     """dispatch -> local_kernel -> combine over ``chunks`` token ranges,
-    alternating over HIP streams (axolotl dispatch_chunked_forward).
-
-    One count pass covers every chunk; with ``exact_counts`` its [C,P] counts
-    reach the host in one copy and size each chunk's buffers, otherwise each
-    chunk gets the worst case T_c * min(K, P) rows.  ``local_kernel(recv_x,
-    recv_idx, recv_w)`` returns the bf16 expert output [rows, H]; it runs on
-    the chunk's stream.  Every chunk's layout is enqueued before chunk 0's
-    expert kernel, and chunk c+1's permute before chunk c's combine result is
-    needed, so the streams overlap; the latency-bound layouts of chunks >= 1
-    run on the second stream while chunk 0's rows stream on the first."""
+    alternating over HIP streams (axolotl dispatch_chunked_forward): one
+    ChunkedDispatcher forward.  ``local_kernel(recv_x, recv_idx, recv_w)``
+    returns the bf16 expert output [rows, H] of one chunk (recv_x is
+    (e4m3 rows, scales) with ``fp8``); it runs on the chunk's stream.  With
+    ``exact_counts`` (the default, as on the page) the split counts of every
+    chunk reach the host in one copy; otherwise each chunk gets the worst
+    case T_c * min(K, P) rows and nothing waits on the host."""
     T, K = topk_idx.shape
-    H = x.shape[1]
-    P = int(num_ranks)
-    dev = x.device
-    main = torch.cuda.current_stream(dev)
-    if streams is None:
-        streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
-    bounds = chunk_bounds(T, chunks)
-    s0 = streams[0]
-    s0.wait_stream(main)
-    c = ep_compute_send_counts(topk_idx, P, num_local_experts, chunks, expert_counts=False,
-                               stream=s0)
-    if exact_counts:
-        with torch.cuda.stream(s0):
-            caps = [int(v) for v in to_host(c.send_counts).sum(dim=1)]
-    else:
-        caps = [(e - s) * min(K, P) for s, e in bounds]
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ready = torch.cuda.Event()
-    ready.record(s0)
-    for st in streams[1:]:
-        st.wait_event(ready)
-    # Layouts: chunk 0's on stream 0, the later chunks' back to back on
-    # stream 1 while chunk 0's permute runs (they are latency-bound).
-    lays, laid = [], []
-    for i, (s, e) in enumerate(bounds):
-        st = s0 if i == 0 or len(streams) == 1 else streams[1]
-        lay = None
-        if e > s:
-            lay = ep_build_send_layout(topk_idx[s:e], topk_weights[s:e], c.dest[s:e],
-                                       c.send_counts[i], P, num_local_experts, caps[i],
-                                       stream=st)
-        ev = torch.cuda.Event()
-        ev.record(st)
-        lays.append(lay)
-        laid.append(ev)
-    for i, (s, e) in enumerate(bounds):
-        if e == s:
-            continue
-        st = streams[i % len(streams)]
-        st.wait_event(laid[i])
-        with torch.cuda.stream(st):
-            lay = lays[i]
-            recv_x = ep_dispatch_permute(x[s:e], lay.token_row, caps[i], fp8=fp8, stream=st)
-            y = local_kernel(recv_x, lay.send_idx, lay.send_w)
-            ep_combine(y, lay.token_row, topk_weights[s:e], out=out[s:e], stream=st)
-    for st in streams:
-        done = torch.cuda.Event()
-        done.record(st)
-        main.wait_event(done)
-    return out
+    d = ChunkedDispatcher(T, K, x.shape[1], num_local_experts=num_local_experts,
+                          num_ranks=num_ranks, chunks=chunks, fp8=fp8,
+                          streams=streams if streams is not None else 2,
+                          exact_counts=exact_counts, device=x.device)
+    return d.forward(x, topk_idx, topk_weights,
+                     lambda i, rx, ri, rw: local_kernel(rx, ri, rw))
 
 
 def batched_prepare(a1: torch.Tensor, topk_ids: torch.Tensor, *, num_local_experts: int,

@@ -40,6 +40,7 @@ __all__ = [
     "workspace_for",
     "ep_workspace_status",
     "check_workspaces",
+    "workspace_flags",
     "WaitGaveUpError",
 ]
 
@@ -166,10 +167,11 @@ def _raise_on_flags(found):
                               f"are undefined: {what}")
 
 
-def check_workspaces(*workspaces: torch.Tensor) -> None:
-    """Query the given workspaces (default: every workspace ``workspace_for``
-    has handed out, each on its own stream) and raise WaitGaveUpError if any
-    recorded a give-up since its last query.  Synchronizes those streams."""
+def workspace_flags(*workspaces: torch.Tensor):
+    """[(flags, kind, device index)] of the given workspaces (default: every
+    workspace ``workspace_for`` has handed out, each queried on its own
+    stream), each read and cleared by ep_workspace_status.  Synchronizes
+    those streams."""
     found = []
     if workspaces:
         for ws in workspaces:
@@ -180,7 +182,14 @@ def check_workspaces(*workspaces: torch.Tensor) -> None:
         while _RETIRED:
             (dev, _, kind), (ws, s) = _RETIRED.pop()
             found.append((ep_workspace_status(ws, stream=s), kind, dev))
-    _raise_on_flags(found)
+    return found
+
+
+def check_workspaces(*workspaces: torch.Tensor) -> None:
+    """Raise WaitGaveUpError if any of the given workspaces (default: all
+    that ``workspace_for`` handed out) recorded a give-up since its last
+    query (see workspace_flags)."""
+    _raise_on_flags(workspace_flags(*workspaces))
 
 
 # ---------------------------------------------------------------------------

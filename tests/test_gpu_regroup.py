@@ -134,44 +134,47 @@ def test_regroup_all_destination_segments_at_once(name, T, H, align):
 
 def test_regroup_expert_major_workload_full_size():
     """The expert-major workload as the bench times it (T=16384, every
-    destination segment of the send buffer at once, align 128), checked by
-    properties that fix the result at any size: counts are the per-(group,
-    expert) bincount, offsets the aligned exclusive scan, each segment holds
-    the rows naming its bin in ascending order then padding, row_map points
-    back at them, and the rows and weights are the sources' (sampled)."""
+    destination segment of the send buffer regrouped in one call, align
+    128), compared element by element with the oracle.  The one call is the
+    regroups of the P segments one after the other (bins are (segment,
+    expert), segment-major), so the oracle regroups each segment on its own
+    and the GPU's result is checked piece by piece: rows, sources (offset by
+    the segment's first row), weights, counts, offsets and row_map."""
     s = spec("expert_major_t16384")
+    print(f"case: full-size expert_major_t16384 T={s.T} H={s.H} P={s.P} align={s.align}",
+          flush=True)
     idx, w = make_routing(s)
     x = make_hidden(s)
     P, El, A, T, K, H = s.P, s.E_local, s.align, s.T, s.K, s.H
     c, lay = ep.ep_dispatch_layout(to_dev(idx), to_dev(w), P, El, T * min(K, P))
     N = int(host(c.send_counts).sum())
     send_x = ep.ep_dispatch_permute(to_dev(x), lay.token_row, T * min(K, P))
-    sti, srk = host(lay.send_token_idx)[:N], host(lay.send_rank)[:N]
-    sidx, sw = host(lay.send_idx)[:N], host(lay.send_w)[:N]
     B = P * El
     out = ep.ep_regroup_by_expert(send_x[:N], lay.send_idx[:N], lay.send_w[:N], El, A,
                                   T * K + B * (A - 1), row_group=lay.send_rank[:N],
                                   num_groups=P)
+    torch.cuda.synchronize()
+    ep.check_workspaces()
+    del send_x
+    sti, srk, sidx, sw, trow = O.build_send_layout(idx, w, P, El)
+    assert len(sti) == N
+    assert np.array_equal(host(lay.send_idx)[:N], sidx)
     cnt, off = host(out.tokens_per_expert), host(out.expert_offsets)
     src, pw, rmap = host(out.perm_src), host(out.perm_w), host(out.row_map)
-    bins = np.where(sidx >= 0, srk[:, None] * El + sidx, -1)
-    assert np.array_equal(cnt, np.bincount(bins[bins >= 0], minlength=B))
-    padded = -(-cnt.astype(np.int64) // A) * A
-    assert np.array_equal(off, np.concatenate([[0], np.cumsum(padded)]))
     M = int(off[-1])
-    for b in range(B):
-        rows = np.flatnonzero((bins == b).any(axis=1))
-        seg = src[off[b]:off[b + 1]]
-        assert np.array_equal(seg[:cnt[b]], rows), b
-        assert np.all(seg[cnt[b]:] == -1)
-        k_of = np.argmax(bins[rows] == b, axis=1)
-        assert np.array_equal(rmap[rows, k_of], off[b] + np.arange(cnt[b]))
-        assert np.array_equal(pw[off[b]:off[b] + cnt[b]].view(np.uint32),
-                              sw[rows, k_of].view(np.uint32))
-    assert np.all(rmap[bins < 0] == -1)
-    rng = np.random.default_rng(4)
-    pick = rng.choice(M, size=400, replace=False)
-    px = bits(out.perm_x[torch.from_numpy(pick).to("cuda")])
-    for j, n in enumerate(pick):
-        want = x[sti[src[n]]] if src[n] >= 0 else np.zeros(H, np.uint16)
-        assert np.array_equal(px[j], want), n
+    px = bits(out.perm_x[:M])
+    del out
+    seg = np.concatenate([[0], np.cumsum(np.bincount(srk, minlength=P))])
+    for p in range(P):
+        r0, r1 = int(seg[p]), int(seg[p + 1])
+        ox = O.dispatch_permute(x, sti[r0:r1])
+        opx, osrc, ow, ocnt, ooff, ormap = O.regroup_by_expert(ox, sidx[r0:r1], sw[r0:r1], El, A)
+        base = int(off[p * El])
+        m = int(ooff[-1])
+        assert np.array_equal(cnt[p * El:(p + 1) * El], ocnt), p
+        assert np.array_equal(off[p * El:(p + 1) * El + 1] - base, ooff), p
+        assert np.array_equal(src[base:base + m], np.where(osrc >= 0, osrc + r0, -1)), p
+        assert np.array_equal(pw[base:base + m].view(np.uint32), ow.view(np.uint32)), p
+        assert np.array_equal(rmap[r0:r1], np.where(ormap >= 0, ormap + base, -1)), p
+        assert np.array_equal(px[base:base + m], opx), p
+    print(f"  N={N} rows regrouped into M={M} rows, every one compared", flush=True)
