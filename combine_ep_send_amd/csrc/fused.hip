@@ -36,7 +36,10 @@ namespace epdc {
 
 namespace {
 
-constexpr uint32_t kBarrierSpinLimit = 1u << 22;   // sleeps (~0.1 s), then give up
+// Polls before a barrier wait gives up: each is an agent-scope load plus a
+// short sleep, about 1.2 s in all on MI355X (measured with every workgroup
+// waiting on a target set past reach).
+constexpr uint32_t kBarrierSpinLimit = 1u << 22;
 
 // Grid-wide barrier number k (1, 2, ...) of this launch.  The arrivals word
 // counts on across calls: `base` is its value when the launch began (the

@@ -28,7 +28,9 @@ namespace epdc {
 
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 22;   // sleeps per lookback window (~0.1 s)
+// Polls per lookback window before the wait gives up (each an agent-scope
+// load of the window plus a short sleep: on the order of a second).
+constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kLookGroup = 8;               // bins whose lookback loads a wave overlaps
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
