@@ -67,6 +67,13 @@ def bytes_dispatch_layout(T, K, P, E, N):
     return 12 * T * K + 4 * T * K + T * P + 4 * (P + E) + N * (8 + 8 * K) + 4 * T * K
 
 
+def bytes_dispatch_layout_chunked(T, K, P, C, N):
+    # counts of C chunks and every chunk's layout in one launch: reads ids +
+    # weights, writes dest, is_in_rank, the [C, P] counts, the send rows'
+    # metadata and token_row (no expert counts)
+    return 12 * T * K + 4 * T * K + T * P + 4 * C * P + N * (8 + 8 * K) + 4 * T * K
+
+
 def bytes_permute(H, U, N):
     return 2 * H * U + 2 * H * N
 
@@ -325,10 +332,11 @@ def build_batched_fp8_step(torch, ep, s, d_idx, d_w, d_x):
 
 def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     """The chunked fp8 workload through the library's ChunkedDispatcher, the
-    same object the parity tests run: one count pass, per-chunk send layouts
-    with the worst-case capacity (no host sync), then per chunk on alternating
-    streams the fp8 quantize-permute and the combine.  The identity expert
-    behind fp8 returns y = bf16(decode(q) * scale), built once before timing."""
+    same object the parity tests run: the counts and every chunk's send
+    layout in one launch with the worst-case capacities (no host sync), then
+    per chunk on alternating streams the fp8 quantize-permute and the
+    combine.  The identity expert behind fp8 returns y = bf16(decode(q) *
+    scale), built once before timing."""
     T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, s.chunks
     disp = ep.ChunkedDispatcher(T, K, H, num_local_experts=El, num_ranks=P, chunks=C, fp8=True,
                                 streams=s.streams, exact_counts=False, device=d_x.device)
@@ -356,17 +364,17 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     step()
     torch.cuda.synchronize()
     sc_host = disp.counts.send_counts.cpu().numpy()
-    kb = {"counts": bytes_counts(T, K, P, s.E, C), "layout": 0, "permute_fp8": 0, "combine": 0}
+    kb = {"dispatch_layout": bytes_dispatch_layout_chunked(T, K, P, C, int(sc_host.sum())),
+          "permute_fp8": 0, "combine": 0}
     Ns = []
     for i, (a, b) in enumerate(disp.bounds):
         N = int(sc_host[i].sum())
         U = int(((d_idx[a:b] >= 0).any(dim=1)).sum().item())
         Ns.append(N)
-        kb["layout"] += bytes_layout(b - a, K, P, N)
         kb["permute_fp8"] += bytes_permute_fp8(H, U, N)
         kb["combine"] += bytes_combine(H, b - a, K, N)
-    # per-launch bytes of the chunked kernels: averages over the C launches
-    per_launch = {k: (v / C if k != "counts" else v) for k, v in kb.items()}
+    # per-launch bytes of the per-chunk kernels: averages over the C launches
+    per_launch = {k: (v / C if k != "dispatch_layout" else v) for k, v in kb.items()}
     return step, kb, {"num_send_per_chunk": Ns, "per_launch_bytes": per_launch,
                       "send_counts": sc_host.sum(axis=0).tolist(),
                       "kernel_timing": "chunks serialized on one stream in the per-kernel pass"}
@@ -426,27 +434,29 @@ def cpu_baseline(s, budget_tokens):
         nbytes = bytes_batched(H, T, K, s.E_local, s.max_num_tokens, U_local) + \
             bytes_combine(H, T, K, int(tpe.sum()))
     else:
-        nbytes = 0
+        nbytes, N_all = 0, 0
         for a, b in O.chunk_bounds(T, s.chunks):
             O.compute_send_counts(idx[a:b], s.P, s.E_local, 1)
             sti, srk, sidx, sw, trow = O.build_send_layout(idx[a:b], w[a:b], s.P, s.E_local)
             N = len(sti)
+            N_all += N
             U = int((idx[a:b] >= 0).any(axis=1).sum())
             if s.fp8:
                 q, sc = O.dispatch_permute_fp8(x[a:b], sti)
+                # the identity expert behind fp8 (untimed, as on the GPU)
+                t_prep = time.perf_counter()
                 y = O.dequantize_rows_fp8(q, sc)
+                t0 += time.perf_counter() - t_prep
                 nbytes += bytes_permute_fp8(H, U, N)
             else:
                 y = O.dispatch_permute(x[a:b], sti)
                 nbytes += bytes_permute(H, U, N)
             O.combine(y, trow, w[a:b])
             nbytes += bytes_combine(H, b - a, K, N)
-            if s.chunks > 1:
-                nbytes += bytes_layout(b - a, K, s.P, N)
-            else:        # the GPU step counts the one-launch counts + layout
+            if s.chunks == 1:    # the GPU step counts the one-launch counts + layout
                 nbytes += bytes_dispatch_layout(b - a, K, s.P, s.E, N)
-        if s.chunks > 1:
-            nbytes += bytes_counts(T, K, s.P, s.E, s.chunks)
+        if s.chunks > 1:         # ... and every chunk's counts and layout in one launch
+            nbytes += bytes_dispatch_layout_chunked(T, K, s.P, s.chunks, N_all)
     dt = time.perf_counter() - t0
     return {
         "value": round(nbytes / dt / 1e9, 4),

@@ -39,6 +39,8 @@ from .ops import (  # noqa: F401
     ep_dispatch_layout,
     ep_dispatch_layout_workspace_bytes,
     ep_dispatch_layout_noalloc,
+    ep_dispatch_layout_chunked,
+    ep_dispatch_layout_chunked_workspace_bytes,
     library_scratch_status,
     ep_counts_workspace_bytes,
     ep_dispatch_permute,

@@ -45,6 +45,10 @@ _SIGNATURES = {
                _P, _SZ, _P]),
     "ep_dispatch_layout_noalloc": (
         _I32, [_P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_dispatch_layout_chunked_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "ep_dispatch_layout_chunked": (
+        _I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+               _P, _SZ, _P]),
     "ep_regroup_workspace_bytes": (_SZ, [_I64, _I32]),
     "ep_regroup_by_expert": (
         _I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P,
@@ -62,7 +66,7 @@ _lib = None
 
 
 # EPDC_ABI_VERSION of include/epdc.h that the signatures above follow
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 def header_functions():

@@ -342,6 +342,10 @@ int dispatch_layout_impl(const int64_t* topk_idx, const float* topk_weights, int
   a.out_w = row_words(num_topk, {dest, token_row});
   a.iir_w = num_ranks % 16 == 0 && aligned(is_in_rank, 16) ? 4
             : num_ranks % 8 == 0 && aligned(is_in_rank, 8) ? 2 : 1;
+  a.ndest = num_ranks;
+  a.C = 1;
+  a.chunk = num_tokens;
+  a.hist_e = E;
   a.tiles = sh.tiles;
   a.tiles_per_group = int(sh.per);
   a.waves = sh.waves;
@@ -377,6 +381,81 @@ int ep_dispatch_layout_noalloc(const int64_t* topk_idx, const float* topk_weight
                               num_local_experts, num_send_capacity, dest, is_in_rank, send_counts,
                               tokens_per_expert, diag, send_token_idx, send_rank, send_idx, send_w,
                               token_row, nullptr, 0, true, stream);
+}
+
+size_t ep_dispatch_layout_chunked_workspace_bytes(int64_t num_tokens, int num_ranks,
+                                                  int num_chunks) {
+  if (num_tokens < 0 || num_tokens >= kMaxTokens || num_ranks < 1 || num_chunks < 1) return 0;
+  const int64_t bins = int64_t(num_ranks) * num_chunks;
+  if (bins > EPDC_MAX_BINS) return 0;
+  return fused_ws_bytes(num_tokens, bins, bins + 1);
+}
+
+int ep_dispatch_layout_chunked(const int64_t* topk_idx, const float* topk_weights,
+                               int64_t num_tokens, int num_topk, int num_ranks,
+                               int num_local_experts, int num_chunks, int64_t chunk_capacity,
+                               int32_t* dest, uint8_t* is_in_rank, int32_t* send_counts,
+                               int32_t* diag, int32_t* send_token_idx, int32_t* send_rank,
+                               int32_t* send_idx, float* send_w, int32_t* token_row,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_routing(num_tokens, num_topk, num_ranks, num_local_experts);
+  if (st != EP_OK) return st;
+  if (num_chunks < 1 || chunk_capacity < 0) return EP_ERR_INVALID_ARG;
+  const int64_t bins64 = int64_t(num_ranks) * num_chunks;
+  if (bins64 > EPDC_MAX_BINS) return EP_ERR_UNSUPPORTED;
+  // every row index of the C chunks' arrays, end to end, fits int32
+  const int64_t rows = chunk_capacity * num_chunks;
+  if (rows > INT32_MAX || rows * num_topk > INT32_MAX) return EP_ERR_UNSUPPORTED;
+  const int64_t TK = num_tokens * num_topk;
+  if (!arr_ok(topk_idx, TK, 8) || !arr_ok(topk_weights, TK, 4) || !arr_ok(dest, TK, 4) ||
+      !arr_ok(is_in_rank, num_tokens * num_ranks, 4) || !arr_ok(send_counts, 1, 4) ||
+      !arr_ok(token_row, TK, 4) || !arr_ok(send_token_idx, rows, 4) ||
+      !arr_ok(send_rank, rows, 4) || !arr_ok(send_idx, rows, 4) || !arr_ok(send_w, rows, 4) ||
+      (diag && !aligned(diag, 4)))
+    return EP_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes <
+          ep_dispatch_layout_chunked_workspace_bytes(num_tokens, num_ranks, num_chunks))
+    return EP_ERR_WORKSPACE;
+  const int bins = int(bins64);
+  const FusedShape sh = fused_shape(num_tokens, bins, 0);
+  if (!sh.fits) return EP_ERR_UNSUPPORTED;
+
+  FusedArgs a{};
+  a.topk_idx = topk_idx;
+  a.topk_weights = topk_weights;
+  a.T = num_tokens;
+  a.K = num_topk;
+  a.P = bins;
+  a.E_local = num_local_experts;
+  a.E = num_ranks * num_local_experts;
+  a.capacity = chunk_capacity;
+  a.dest = dest;
+  a.is_in_rank = is_in_rank;
+  a.send_counts = send_counts;
+  a.tokens_per_expert = nullptr;
+  a.diag = diag;
+  a.send_token_idx = send_token_idx;
+  a.send_rank = send_rank;
+  a.send_idx = send_idx;
+  a.send_w = send_w;
+  a.token_row = token_row;
+  // rows are K words apart, so every row (chunk c's from row c*capacity on)
+  // is as aligned as the arrays' bases for the whole-row forms
+  a.rows_w = row_words(num_topk, {send_idx, send_w});
+  a.in_w = aligned(topk_idx, 16) ? row_words(num_topk, {topk_weights}) : 1;
+  a.out_w = row_words(num_topk, {dest, token_row});
+  a.iir_w = num_ranks % 16 == 0 && aligned(is_in_rank, 16) ? 4
+            : num_ranks % 8 == 0 && aligned(is_in_rank, 8) ? 2 : 1;
+  a.ndest = num_ranks;
+  a.C = num_chunks;
+  a.chunk = num_tokens / num_chunks;
+  a.hist_e = 0;
+  a.tiles = sh.tiles;
+  a.tiles_per_group = int(sh.per);
+  a.waves = sh.waves;
+  set_fused_workspace(a, workspace, bins, int64_t(bins) + 1, sh.groups);
+  return launch_status(launch_dispatch_layout(a, unsigned(sh.groups), stream));
 }
 
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins) {
@@ -430,6 +509,10 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   a.E = 0;
   a.row_group = num_groups > 1 ? row_group : nullptr;
   a.capacity = capacity;
+  a.ndest = bins;
+  a.C = 1;
+  a.chunk = num_rows;
+  a.hist_e = 0;
   a.send_counts = tokens_per_expert;
   a.send_token_idx = perm_src;
   a.token_row = row_map;

@@ -103,6 +103,14 @@ struct FusedArgs {
   uint32_t* pref;                // [groups, P] per-group exclusive prefixes (two-pass scan)
   uint32_t* tots;                // [P] bin totals (two-pass scan)
   bool two_pass;                 // scan the rows bin by bin, with a second barrier
+  // Chunks (send mode): the bins are (chunk, destination), chunk-major, with
+  // P = C * ndest bins; chunk c = tokens [c*chunk, (c+1)*chunk), the last
+  // chunk ending at T.  Rows are numbered within their chunk (capacity =
+  // rows per chunk) and chunk c's rows are written from row c*capacity.
+  int ndest;                     // destinations (P when C == 1)
+  int C;                         // chunks (>= 1)
+  int64_t chunk;                 // tokens per chunk, T / C
+  int hist_e;                    // expert words in each published row (E, or 0)
   int64_t tiles;                 // tiles of waves*64 tokens (>= 1)
   int tiles_per_group;
   int waves;                     // waves per workgroup: 1, 2 or 4 (one token per thread)

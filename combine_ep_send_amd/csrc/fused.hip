@@ -106,6 +106,8 @@ struct TileSlots {
   int64_t ids[KMAX];
   float wts[KMAX];
   int bad;
+  int cidx;     // chunk of the token (send mode with chunks), else 0
+  int cbase;    // its first bin, cidx * ndest
 };
 
 enum { kFusedSend = 0, kFusedRegroup = 1 };
@@ -114,6 +116,8 @@ template <int MODE, int KMAX>
 __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid,
                                        TileSlots<KMAX>& s) {
   s.bad = 0;
+  s.cidx = 0;
+  s.cbase = 0;
   if (MODE == kFusedRegroup) {
     // received rows: K-wide local expert ids (int32); the bin is the id,
     // offset by the row's group (the receive buffer it came from) when rows
@@ -176,12 +180,18 @@ __device__ __forceinline__ void decode(const FusedArgs& a, int64_t t, bool valid
       }
     }
   }
+  if (a.C > 1 && valid) {       // bins (chunk, destination), chunk-major
+    uint32_t c = a.chunk > 0 ? uint32_t(t) / uint32_t(a.chunk) : uint32_t(a.C - 1);
+    if (c > uint32_t(a.C - 1)) c = uint32_t(a.C - 1);
+    s.cidx = int(c);
+    s.cbase = int(c) * a.ndest;
+  }
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     const int64_t v = s.ids[k];
     s.bin[k] = -1;
     if (v >= 0 && v < a.E)
-      s.bin[k] = int(v) / a.E_local;
+      s.bin[k] = s.cbase + int(v) / a.E_local;
     else if (v != -1)
       ++s.bad;
   }
@@ -227,8 +237,8 @@ template <int MODE, int KMAX, int NW>
 __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a) {
   constexpr int BS = NW * kWave;        // threads per workgroup = tokens per tile
   extern __shared__ __align__(16) unsigned char smem[];
-  const int P = a.P;
-  const int nh = a.P + a.E + 1;                 // published row: P dests, E experts, bad
+  const int P = a.P;                            // bins: destinations (x chunks)
+  const int nh = a.P + a.hist_e + 1;            // published row: P bins, experts, bad
   uint64_t* s_bal = reinterpret_cast<uint64_t*>(smem);                        // [4][P]
   int32_t* s_woff = reinterpret_cast<int32_t*>(s_bal + NW * P);             // [NW][P]
   int32_t* s_tcnt = s_woff + NW * P;                                         // [tpw][P]
@@ -263,26 +273,30 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
     const bool valid = t < a.T;
     decode<MODE, KMAX>(a, t, valid, sl);
     if (MODE == kFusedSend && valid) {
-      store_row<KMAX>(a.dest + t * a.K, sl.bin, a.K, a.out_w);
+      int dv[KMAX];                             // owning destination, or -1
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) dv[k] = sl.bin[k] >= 0 ? sl.bin[k] - sl.cbase : -1;
+      store_row<KMAX>(a.dest + t * a.K, dv, a.K, a.out_w);
       // membership row: 16 or 8 destinations per store when the rows allow
-      // it, else 4 per 32-bit store (P % 4 == 0) or bytes
-      uint8_t* row = a.is_in_rank + t * P;
+      // it, else 4 per 32-bit store (ndest % 4 == 0) or bytes
+      const int D = a.ndest;
+      uint8_t* row = a.is_in_rank + t * D;
       const int step = a.iir_w == 4 ? 16 : (a.iir_w == 2 ? 8 : 4);
-      for (int p0 = 0; p0 < P; p0 += step) {
+      for (int p0 = 0; p0 < D; p0 += step) {
         uint32_t word[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-          const int d = sl.bin[k] - p0;
+          const int d = dv[k] - p0;
           if (d >= 0 && d < step) word[d >> 2] |= 1u << (8 * (d & 3));
         }
         if (a.iir_w == 4) {
           *reinterpret_cast<u32x4*>(row + p0) = u32x4{word[0], word[1], word[2], word[3]};
         } else if (a.iir_w == 2) {
           *reinterpret_cast<u32x2*>(row + p0) = u32x2{word[0], word[1]};
-        } else if ((P & 3) == 0) {
+        } else if ((D & 3) == 0) {
           *reinterpret_cast<uint32_t*>(row + p0) = word[0];
         } else {
-          for (int q = 0; q < 4 && p0 + q < P; ++q) row[p0 + q] = uint8_t((word[0] >> (8 * q)) & 1u);
+          for (int q = 0; q < 4 && p0 + q < D; ++q) row[p0 + q] = uint8_t((word[0] >> (8 * q)) & 1u);
         }
       }
     }
@@ -438,26 +452,31 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
     if (tid == 0 && a.diag) a.diag[0] = s_bad;
   }
   // Segment starts (exclusive scan of the totals, each rounded up to the
-  // alignment when regrouping) added into the bases.
+  // alignment when regrouping) added into the bases.  With chunks the scan
+  // restarts at each chunk's first bin: a chunk's rows are numbered on
+  // their own.
   if (wave == 0) {
-    int carry = 0;
-    for (int b0 = 0; b0 < P; b0 += kWave) {
-      const int b = b0 + lane;
-      int v = b < P ? s_tot[b] : 0;
-      if (MODE == kFusedRegroup) v = (v + a.align - 1) / a.align * a.align;
-      int incl = v;
+    const int span = a.C > 1 ? a.ndest : P;
+    for (int r0 = 0; r0 < P; r0 += span) {
+      int carry = 0;
+      for (int b0 = r0; b0 < r0 + span; b0 += kWave) {
+        const int b = b0 + lane;
+        int v = b < r0 + span ? s_tot[b] : 0;
+        if (MODE == kFusedRegroup) v = (v + a.align - 1) / a.align * a.align;
+        int incl = v;
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int u = __shfl_up(incl, off);
-        if (lane >= off) incl += u;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int u = __shfl_up(incl, off);
+          if (lane >= off) incl += u;
+        }
+        if (b < r0 + span) {
+          s_base[b] += carry + incl - v;
+          if (MODE == kFusedRegroup && g == 0) a.offsets[b] = carry + incl - v;
+        }
+        carry += __shfl(incl, kWave - 1);
       }
-      if (b < P) {
-        s_base[b] += carry + incl - v;
-        if (MODE == kFusedRegroup && g == 0) a.offsets[b] = carry + incl - v;
-      }
-      carry += __shfl(incl, kWave - 1);
+      if (MODE == kFusedRegroup && g == 0 && lane == 0) a.offsets[P] = carry;
     }
-    if (MODE == kFusedRegroup && g == 0 && lane == 0) a.offsets[P] = carry;
   }
   __syncthreads();
 
@@ -505,11 +524,14 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
         if (a.perm_w) a.perm_w[n] = sl.wts[k];
         continue;
       }
-      a.send_token_idx[n] = int32_t(t);
-      a.send_rank[n] = b;
-      const int64_t ob = int64_t(b) * a.E_local;
-      int32_t* irow = a.send_idx + int64_t(n) * a.K;
-      float* wrow = a.send_w + int64_t(n) * a.K;
+      // chunk c's rows start at row c * capacity; its tokens count from the
+      // chunk's first token
+      const int64_t row = int64_t(sl.cidx) * a.capacity + n;
+      a.send_token_idx[row] = int32_t(t - int64_t(sl.cidx) * a.chunk);
+      a.send_rank[row] = b - sl.cbase;
+      const int64_t ob = int64_t(b - sl.cbase) * a.E_local;
+      int32_t* irow = a.send_idx + row * a.K;
+      float* wrow = a.send_w + row * a.K;
 #pragma unroll
       for (int kk = 0; kk < KMAX; kk += 4) {
         if (kk >= a.K) break;
@@ -576,7 +598,7 @@ void launch_fused_nw(const FusedArgs& a, unsigned groups, size_t smem, hipStream
 
 template <int MODE>
 hipError_t launch_fused(const FusedArgs& a, unsigned groups, hipStream_t s) {
-  const size_t smem = fused_smem_bytes(a.P, a.E, a.tiles_per_group, a.waves);
+  const size_t smem = fused_smem_bytes(a.P, a.hist_e, a.tiles_per_group, a.waves);
   if (a.waves == 1)
     launch_fused_nw<MODE, 1>(a, groups, smem, s);
   else if (a.waves == 2)

@@ -14,7 +14,8 @@ import torch
 
 from .ops import (Counts, Regrouped, SendLayout, ep_batched_prepare, ep_batched_prepare_fp8,
                   ep_build_send_layout, ep_combine, ep_compute_send_counts,
-                  ep_counts_workspace_bytes, ep_dispatch_layout, ep_dispatch_permute,
+                  ep_counts_workspace_bytes, ep_dispatch_layout, ep_dispatch_layout_chunked,
+                  ep_dispatch_layout_chunked_workspace_bytes, ep_dispatch_permute,
                   ep_layout_workspace_bytes, ep_regroup_by_expert, workspace_for)
 
 __all__ = [
@@ -142,18 +143,20 @@ class ChunkedDispatcher:
     the streams, so repeated forwards allocate nothing but events.
 
     One forward, in enqueue order:
-      1. stream 0 waits for the caller's stream and counts every chunk in one
-         pass ([C, P] send counts);
-      2. with ``exact_counts`` the counts reach the host in ONE copy and size
-         each chunk exactly; otherwise each chunk gets its worst case
-         T_c * min(K, P) rows and nothing waits on the host;
-      3. the send layouts: chunk 0's on stream 0, the later chunks' back to
-         back on stream 1 (they are latency-bound, and run while chunk 0's
+      1. stream 0 waits for the caller's stream;
+      2. without ``exact_counts``: the counts of every chunk and all the
+         chunks' send layouts in ONE launch on stream 0
+         (ep_dispatch_layout_chunked), each chunk with its worst case
+         T_c * min(K, P) rows, so nothing waits on the host;
+         with ``exact_counts``: one count pass over every chunk ([C, P]),
+         the counts reach the host in ONE copy and size each chunk exactly,
+         then the send layouts, chunk 0's on stream 0 and the later chunks'
+         back to back on stream 1 (latency-bound, they run while chunk 0's
          rows stream);
-      4. chunk c on stream c mod S: the row permute, ``local_kernel(c,
+      3. chunk c on stream c mod S: the row permute, ``local_kernel(c,
          recv_x, recv_idx, recv_w)`` (bf16 expert output [rows, H], enqueued
          on that stream), then the weighted combine into out[start:end];
-      5. the caller's stream waits for every stream.
+      4. the caller's stream waits for every stream.
     Chunk c+1's permute is enqueued before chunk c's combine is consumed.
     ``timer`` (start(name, stream) / stop(token)) brackets every launch with
     events; ``serialize`` puts all of it on stream 0."""
@@ -175,8 +178,9 @@ class ChunkedDispatcher:
             raise ValueError("at least one stream")
         self.streams = list(streams)
         self.bounds = chunk_bounds(self.T, self.C)
-        self.worst = [(e - s) * min(self.K, self.P) for s, e in self.bounds]
-        self.caps = list(self.worst)
+        # one row stride for every chunk: the largest chunk's worst case
+        self.stride = max((e - s) * min(self.K, self.P) for s, e in self.bounds)
+        self.caps = [self.stride] * self.C
         T, K, P, H = self.T, self.K, self.P, self.H
         s0 = self.streams[0]
         self.counts = Counts(
@@ -185,25 +189,36 @@ class ChunkedDispatcher:
             send_counts=torch.empty((self.C, P), dtype=torch.int32, device=dev),
             tokens_per_expert=None,
             diag=torch.empty(1, dtype=torch.int32, device=dev))
-        self.ws_counts = workspace_for(ep_counts_workspace_bytes(T, P, self.El, self.C), dev, s0,
-                                       "counts")
+        # every chunk's layout in one set of arrays (chunk c's rows from row
+        # c * stride), each chunk's layout a view of it
+        cap, rows = self.stride, self.stride * self.C
+        self.all_layouts = SendLayout(
+            send_token_idx=torch.empty(rows, dtype=torch.int32, device=dev),
+            send_rank=torch.empty(rows, dtype=torch.int32, device=dev),
+            send_idx=torch.empty((rows, K), dtype=torch.int32, device=dev),
+            send_w=torch.empty((rows, K), dtype=torch.float32, device=dev),
+            token_row=torch.empty((T, K), dtype=torch.int32, device=dev))
+        if self.exact_counts:
+            self.ws_counts = workspace_for(ep_counts_workspace_bytes(T, P, self.El, self.C), dev,
+                                           s0, "counts")
+        else:
+            self.ws_fused = workspace_for(ep_dispatch_layout_chunked_workspace_bytes(T, P, self.C),
+                                          dev, s0, "fused")
+        L = self.all_layouts
         self.layouts, self.recv, self.ws_layout = [], [], []
-        for i, cap in enumerate(self.worst):
-            self.layouts.append(SendLayout(
-                send_token_idx=torch.empty(cap, dtype=torch.int32, device=dev),
-                send_rank=torch.empty(cap, dtype=torch.int32, device=dev),
-                send_idx=torch.empty((cap, K), dtype=torch.int32, device=dev),
-                send_w=torch.empty((cap, K), dtype=torch.float32, device=dev),
-                token_row=torch.empty((self.bounds[i][1] - self.bounds[i][0], K),
-                                      dtype=torch.int32, device=dev)))
+        for i, (a, b) in enumerate(self.bounds):
+            r = slice(i * cap, (i + 1) * cap)
+            self.layouts.append(SendLayout(L.send_token_idx[r], L.send_rank[r], L.send_idx[r],
+                                           L.send_w[r], L.token_row[a:b]))
             if self.fp8:
                 self.recv.append((torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev),
                                   torch.empty((cap, H // 128), dtype=torch.float32, device=dev)))
             else:
                 self.recv.append(torch.empty((cap, H), dtype=torch.bfloat16, device=dev))
-            n = self.bounds[i][1] - self.bounds[i][0]
-            st = self._layout_stream(i, False)
-            self.ws_layout.append(workspace_for(ep_layout_workspace_bytes(max(n, 1), P), dev, st))
+            if self.exact_counts:
+                st = self._layout_stream(i, False)
+                self.ws_layout.append(workspace_for(ep_layout_workspace_bytes(max(b - a, 1), P),
+                                                    dev, st))
 
     def _layout_stream(self, i: int, serialize: bool):
         if serialize or i == 0 or len(self.streams) == 1:
@@ -233,29 +248,40 @@ class ChunkedDispatcher:
         start = torch.cuda.Event()
         start.record(main)
         s0.wait_event(start)
-        tk = mark("counts", s0)
-        ep_compute_send_counts(topk_idx, P, El, self.C, expert_counts=False, out=self.counts,
-                               workspace=self.ws_counts, stream=s0)
-        done(tk)
-        if self.exact_counts:
+        laid = []
+        if not self.exact_counts:
+            # counts and every chunk's layout in one launch, no host sync
+            tk = mark("dispatch_layout", s0)
+            ep_dispatch_layout_chunked(topk_idx, topk_weights, P, El, self.C, self.stride,
+                                       counts=self.counts, out=self.all_layouts,
+                                       workspace=self.ws_fused, stream=s0)
+            done(tk)
+            ready = torch.cuda.Event()
+            ready.record(s0)
+            laid = [(ready, s0)] * self.C
+        else:
+            tk = mark("counts", s0)
+            ep_compute_send_counts(topk_idx, P, El, self.C, expert_counts=False,
+                                   out=self.counts, workspace=self.ws_counts, stream=s0)
+            done(tk)
             with torch.cuda.stream(s0):
                 self.caps = [int(v) for v in to_host(self.counts.send_counts).sum(dim=1)]
-        ready = torch.cuda.Event()
-        ready.record(s0)
-        for st in streams[1:]:
-            st.wait_event(ready)
-        laid = []
-        for i, (a, b) in enumerate(self.bounds):
-            st = self._layout_stream(i, serialize)
-            if b > a:
-                tk = mark("layout", st)
-                ep_build_send_layout(topk_idx[a:b], topk_weights[a:b], self.counts.dest[a:b],
-                                     self.counts.send_counts[i], P, El, self.caps[i],
-                                     out=self.layouts[i], workspace=self.ws_layout[i], stream=st)
-                done(tk)
-            ev = torch.cuda.Event()
-            ev.record(st)
-            laid.append((ev, st))
+            ready = torch.cuda.Event()
+            ready.record(s0)
+            for st in streams[1:]:
+                st.wait_event(ready)
+            for i, (a, b) in enumerate(self.bounds):
+                st = self._layout_stream(i, serialize)
+                if b > a:
+                    tk = mark("layout", st)
+                    ep_build_send_layout(topk_idx[a:b], topk_weights[a:b], self.counts.dest[a:b],
+                                         self.counts.send_counts[i], P, El, self.caps[i],
+                                         out=self.layouts[i], workspace=self.ws_layout[i],
+                                         stream=st)
+                    done(tk)
+                ev = torch.cuda.Event()
+                ev.record(st)
+                laid.append((ev, st))
         for i, (a, b) in enumerate(self.bounds):
             if b == a:
                 continue

@@ -24,6 +24,8 @@ __all__ = [
     "ep_dispatch_layout",
     "ep_dispatch_layout_workspace_bytes",
     "ep_dispatch_layout_noalloc",
+    "ep_dispatch_layout_chunked",
+    "ep_dispatch_layout_chunked_workspace_bytes",
     "library_scratch_status",
     "ep_dispatch_permute",
     "ep_regroup_by_expert",
@@ -393,6 +395,70 @@ def library_scratch_status(*, stream=None) -> int:
     check(st, "ep_workspace_status")
     s.synchronize()
     return int(flags.item())
+
+
+def ep_dispatch_layout_chunked_workspace_bytes(num_tokens: int, num_ranks: int,
+                                               num_chunks: int) -> int:
+    return int(lib().ep_dispatch_layout_chunked_workspace_bytes(int(num_tokens), int(num_ranks),
+                                                                int(num_chunks)))
+
+
+def ep_dispatch_layout_chunked(topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+                               num_ranks: int, num_local_experts: int, num_chunks: int,
+                               chunk_capacity: int, *, counts: Optional[Counts] = None,
+                               out: Optional[SendLayout] = None,
+                               workspace: Optional[torch.Tensor] = None, stream=None):
+    """Counts of every chunk and every chunk's send layout in one launch.
+    Returns (Counts with C chunks and no expert counts, SendLayout whose
+    send arrays hold C * chunk_capacity rows, chunk c's from row
+    c * chunk_capacity, and whose token_row holds chunk-local rows)."""
+    _gpu(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    P, El, C, cap = int(num_ranks), int(num_local_experts), int(num_chunks), int(chunk_capacity)
+    rows = C * cap
+    _shape(_gpu(topk_weights, "topk_weights", torch.float32), "topk_weights", (T, K))
+    dev = topk_idx.device
+    if counts is None:
+        counts = Counts(
+            dest=torch.empty((T, K), dtype=torch.int32, device=dev),
+            is_in_rank=torch.empty((T, P), dtype=torch.uint8, device=dev),
+            send_counts=torch.empty((C, P), dtype=torch.int32, device=dev),
+            tokens_per_expert=None,
+            diag=torch.empty(1, dtype=torch.int32, device=dev))
+    if counts.tokens_per_expert is not None:
+        raise ValueError("ep_dispatch_layout_chunked gives no expert counts")
+    _shape(_gpu(counts.dest, "dest", torch.int32), "dest", (T, K))
+    _shape(_gpu(counts.is_in_rank, "is_in_rank", torch.uint8), "is_in_rank", (T, P))
+    _shape(_gpu(counts.send_counts, "send_counts", torch.int32), "send_counts", (C, P))
+    _shape(_gpu(counts.diag, "diag", torch.int32), "diag", (1,))
+    if out is None:
+        out = SendLayout(
+            send_token_idx=torch.empty(rows, dtype=torch.int32, device=dev),
+            send_rank=torch.empty(rows, dtype=torch.int32, device=dev),
+            send_idx=torch.empty((rows, K), dtype=torch.int32, device=dev),
+            send_w=torch.empty((rows, K), dtype=torch.float32, device=dev),
+            token_row=torch.empty((T, K), dtype=torch.int32, device=dev))
+    for name, t, dt in (("send_token_idx", out.send_token_idx, torch.int32),
+                        ("send_rank", out.send_rank, torch.int32),
+                        ("send_idx", out.send_idx, torch.int32),
+                        ("send_w", out.send_w, torch.float32)):
+        _gpu(t, name, dt)
+        if t.shape[0] < rows:
+            raise ValueError(f"{name} holds fewer than {rows} rows")
+    if out.send_idx.dim() != 2 or out.send_idx.shape[1] != K or out.send_w.shape[1:] != (K,):
+        raise ValueError("send_idx / send_w must be [rows, K]")
+    _shape(_gpu(out.token_row, "token_row", torch.int32), "token_row", (T, K))
+    if workspace is None:
+        workspace = workspace_for(ep_dispatch_layout_chunked_workspace_bytes(T, P, C), dev,
+                                  stream, "fused")
+    _gpu(workspace, "workspace", torch.uint8)
+    st = lib().ep_dispatch_layout_chunked(
+        _vp(topk_idx), _vp(topk_weights), T, K, P, El, C, cap, _vp(counts.dest),
+        _vp(counts.is_in_rank), _vp(counts.send_counts), _vp(counts.diag),
+        _vp(out.send_token_idx), _vp(out.send_rank), _vp(out.send_idx), _vp(out.send_w),
+        _vp(out.token_row), _vp(workspace), workspace.numel(), _stream(stream))
+    check(st, "ep_dispatch_layout_chunked")
+    return counts, out
 
 
 def ep_regroup_workspace_bytes(num_rows: int, num_bins: int) -> int:

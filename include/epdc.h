@@ -51,7 +51,7 @@
  *  - Workspaces: each serves one family of calls, whose control words it
  *    keeps: ep_compute_send_counts; the scans (ep_build_send_layout,
  *    ep_batched_prepare, ep_batched_prepare_fp8); or the one-launch layouts
- *    (ep_dispatch_layout, ep_regroup_by_expert).  Zero it once, size it for
+ *    (ep_dispatch_layout, ep_dispatch_layout_chunked, ep_regroup_by_expert).  Zero it once, size it for
  *    the largest call, and do not hand it to a call of another family or to
  *    two calls that may run at the same time.  The ep_*_workspace_bytes
  *    functions return 0 for negative or zero sizes and for T >= 2^30 or
@@ -87,7 +87,7 @@ typedef enum {
     EP_SCALE_UE8M0 = 2         /* that power as a UE8M0 byte, 4 per int32 */
 } ep_scale_fmt_t;
 
-#define EPDC_ABI_VERSION 5
+#define EPDC_ABI_VERSION 6
 #define EPDC_MAX_TOPK 16
 #define EPDC_MAX_BINS 1024
 #define EPDC_FP8_GROUP 128
@@ -301,6 +301,49 @@ int ep_dispatch_layout_noalloc(const int64_t* topk_idx, const float* topk_weight
                                int32_t* send_token_idx, int32_t* send_rank,
                                int32_t* send_idx, float* send_w, int32_t* token_row,
                                hipStream_t stream);
+
+/*
+ * Bytes of workspace ep_dispatch_layout_chunked needs: as
+ * ep_dispatch_layout's with C*P bins and no expert totals (G rows of
+ * C*P + 1 uint32, G rows of C*P uint32 and C*P uint32 after the 256-byte
+ * header).  0 for invalid sizes or C*P > 1024.
+ */
+size_t ep_dispatch_layout_chunked_workspace_bytes(int64_t num_tokens, int num_ranks,
+                                                  int num_chunks);
+
+/*
+ * The counts of every chunk and the send layouts of all chunks in one
+ * launch (the no-sync path of a chunked dispatch).
+ * axolotl "torch_dispatch": chunk_bounds, dispatch_chunked_forward (the
+ * split counts of every chunk from one count pass; each chunk dispatched
+ * on its own), compute_send_counts, build_send_layout.
+ *
+ * Chunk c is tokens [c*(T/C), (c+1)*(T/C)), the last chunk ending at T.
+ * The outputs are those of ep_compute_send_counts with C chunks (without
+ * tokens_per_expert) and, for every chunk, those of ep_build_send_layout
+ * on that chunk's tokens with capacity chunk_capacity, laid end to end:
+ *   dest [T,K], is_in_rank [T,P]   as ep_compute_send_counts
+ *   send_counts [C,P]              per chunk and destination
+ *   send_token_idx, send_rank      [C*chunk_capacity] int32: chunk c's rows
+ *   send_idx, send_w               [C*chunk_capacity, K]: from row
+ *                                  c*chunk_capacity on, numbered within the
+ *                                  chunk; send_token_idx counts from the
+ *                                  chunk's first token
+ *   token_row [T,K]                the slot's row within its chunk, -1 for
+ *                                  unrouted slots and rows past the capacity
+ *   diag                           as ep_compute_send_counts (may be NULL)
+ * chunk_capacity >= (tokens of the largest chunk) * min(K, P) always
+ * suffices.  Limits: C*P <= 1024 bins, C*chunk_capacity*K fits int32; the
+ * one-launch rules of ep_dispatch_layout (grid barrier, time-out,
+ * EP_ERR_UNSUPPORTED when the LDS share would pass 64 KiB) apply.
+ */
+int ep_dispatch_layout_chunked(const int64_t* topk_idx, const float* topk_weights,
+                               int64_t num_tokens, int num_topk, int num_ranks,
+                               int num_local_experts, int num_chunks, int64_t chunk_capacity,
+                               int32_t* dest, uint8_t* is_in_rank, int32_t* send_counts,
+                               int32_t* diag, int32_t* send_token_idx, int32_t* send_rank,
+                               int32_t* send_idx, float* send_w, int32_t* token_row,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Bytes of workspace ep_regroup_by_expert needs for R received rows and

@@ -17,6 +17,7 @@ EXPECTED = {
     "ep_abi_version", "ep_status_string", "ep_workspace_status", "ep_counts_workspace_bytes", "ep_layout_workspace_bytes",
     "ep_batched_workspace_bytes", "ep_compute_send_counts", "ep_build_send_layout",
     "ep_dispatch_layout_workspace_bytes", "ep_dispatch_layout", "ep_dispatch_layout_noalloc",
+    "ep_dispatch_layout_chunked_workspace_bytes", "ep_dispatch_layout_chunked",
     "ep_regroup_workspace_bytes", "ep_regroup_by_expert",
     "ep_dispatch_permute", "ep_batched_prepare", "ep_batched_prepare_fp8", "ep_combine",
 }
@@ -43,9 +44,10 @@ def test_bindings_follow_the_header_version():
 
 
 def test_version_and_status_strings():
-    # version 5: ep_dispatch_layout_noalloc (version 4: ep_workspace_status)
+    # version 6: ep_dispatch_layout_chunked (5: ep_dispatch_layout_noalloc,
+    # 4: ep_workspace_status)
     L = _lib.lib()
-    assert L.ep_abi_version() == 5
+    assert L.ep_abi_version() == 6
     assert L.ep_status_string(0) == b"ok"
     for s in (-1, -2, -3, -4):
         assert L.ep_status_string(s) not in (b"ok", b"unknown status")
@@ -155,6 +157,28 @@ def test_fused_layout_workspace_and_arguments():
     assert call(ws_bytes=64) == _lib.EP_ERR_WORKSPACE
     # LDS share over 64 KiB (1024 destinations x 8 experts): use the two calls
     assert call(T=20000, P=1024, El=8) == _lib.EP_ERR_UNSUPPORTED
+
+
+def test_chunked_layout_workspace_and_arguments():
+    L = _lib.lib()
+    # 4 chunks x 32 destinations = 128 bins, 64 workgroups at 16384 tokens
+    assert L.ep_dispatch_layout_chunked_workspace_bytes(16384, 32, 4) == \
+        256 + 64 * (128 + 1) * 4 + 64 * 128 * 4 + 128 * 4
+    assert L.ep_dispatch_layout_chunked_workspace_bytes(16384, 32, 33) == 0     # 1056 bins
+    assert L.ep_dispatch_layout_chunked_workspace_bytes(16, 2, 0) == 0
+    f = L.ep_dispatch_layout_chunked
+
+    def call(T=16, K=2, P=2, El=4, C=2, cap=64, dest=A16, sti=A16, ws=A16, ws_bytes=1 << 22):
+        return f(A16, A16, T, K, P, El, C, cap, dest, A16, A16, None, sti, A16, A16, A16, A16,
+                 ws, ws_bytes, None)
+    assert call(C=0) == _lib.EP_ERR_INVALID_ARG
+    assert call(cap=-1) == _lib.EP_ERR_INVALID_ARG
+    assert call(P=32, C=33) == _lib.EP_ERR_UNSUPPORTED        # more than 1024 bins
+    assert call(C=4, cap=1 << 29, K=2) == _lib.EP_ERR_UNSUPPORTED   # C*cap*K past int32
+    assert call(dest=ODD) == _lib.EP_ERR_INVALID_ARG
+    assert call(sti=None) == _lib.EP_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.EP_ERR_WORKSPACE
+    assert call(ws_bytes=64) == _lib.EP_ERR_WORKSPACE
 
 
 def test_noalloc_layout_rejects_before_touching_the_gpu():

@@ -102,3 +102,19 @@ def test_regroup_bytes_are_the_arrays():
     # each received row read once, every regrouped row written
     want = _nbytes(sidx, sw, srk, row_map, src, pw, tpe, off, recv_x, perm_x)
     assert B.bytes_regroup(H, N, K, M, int((src >= 0).sum()), Bn) == want
+
+
+def test_chunked_one_launch_layout_bytes_are_the_arrays():
+    s = spec("fp8_t32768", T=777, H=512)
+    idx, w = make_routing(s)
+    T, K, P, El, C = s.T, s.K, s.P, s.E_local, s.chunks
+    dest, iir, sc, _ = O.compute_send_counts(idx, P, El, C)
+    rows, N = [], 0
+    for a, b in O.chunk_bounds(T, C):
+        sti, srk, sidx, sw, trow = O.build_send_layout(idx[a:b], w[a:b], P, El)
+        rows += [sti, srk, sidx, sw]
+        N += len(sti)
+    # ids and weights in; dest, membership, the [C, P] counts, every chunk's
+    # send rows' metadata and token_row out
+    want = _nbytes(idx, w, dest, iir, sc, *rows, np.empty((T, K), np.int32))
+    assert B.bytes_dispatch_layout_chunked(T, K, P, C, N) == want

@@ -1,0 +1,112 @@
+"""ep_dispatch_layout_chunked against the oracle: the counts of every chunk
+and every chunk's send layout in one launch (axolotl "torch_dispatch":
+chunk_bounds, dispatch_chunked_forward, compute_send_counts,
+build_send_layout).  Chunk c's rows sit from row c * capacity on and must
+equal the oracle's layout of that chunk's tokens, bit for bit; rows past a
+chunk's count are left untouched."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from epgen import make_routing, spec
+from tests.gpu_helpers import gpu_available, host, to_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+import combine_ep_send_amd as ep  # noqa: E402
+
+SENTINEL = -7
+
+
+def _run(s, C, cap=None, bad_ids=False):
+    idx, w = make_routing(s)
+    if bad_ids:
+        idx = idx.copy()
+        idx[::97, 0] = s.E + 3                 # ids past E: counted in diag, treated as unrouted
+    T, K, P, El = s.T, s.K, s.P, s.E_local
+    worst = max((b - a) * min(K, P) for a, b in O.chunk_bounds(T, C))
+    cap = worst if cap is None else cap
+    print(f"case: chunked layout {s.name} T={T} K={K} P={P} C={C} cap={cap} bad={bad_ids}",
+          flush=True)
+    rows = C * cap
+    dev = "cuda"
+    out = ep.SendLayout(
+        send_token_idx=torch.full((rows,), SENTINEL, dtype=torch.int32, device=dev),
+        send_rank=torch.full((rows,), SENTINEL, dtype=torch.int32, device=dev),
+        send_idx=torch.full((rows, K), SENTINEL, dtype=torch.int32, device=dev),
+        send_w=torch.full((rows, K), float(SENTINEL), dtype=torch.float32, device=dev),
+        token_row=torch.full((T, K), SENTINEL, dtype=torch.int32, device=dev))
+    c, lay = ep.ep_dispatch_layout_chunked(to_dev(idx), to_dev(w), P, El, C, cap, out=out)
+    torch.cuda.synchronize()
+    ep.check_workspaces()
+    return idx, w, cap, c, lay
+
+
+def _check(s, C, idx, w, cap, c, lay, bad=0):
+    T, K, P, El = s.T, s.K, s.P, s.E_local
+    clean = np.where(idx < s.E, idx, -1)       # the oracle's precondition: ids in [-1, E)
+    dest, iir, sc, _ = O.compute_send_counts(clean, P, El, C)
+    assert np.array_equal(host(c.dest), dest)
+    assert np.array_equal(host(c.is_in_rank), iir)
+    assert np.array_equal(host(c.send_counts), sc)
+    assert int(host(c.diag)[0]) == bad
+    g_sti, g_srk = host(lay.send_token_idx), host(lay.send_rank)
+    g_sidx, g_sw, g_trow = host(lay.send_idx), host(lay.send_w), host(lay.token_row)
+    for i, (a, b) in enumerate(O.chunk_bounds(T, C)):
+        sti, srk, sidx, sw, trow = O.build_send_layout(clean[a:b], w[a:b], P, El)
+        n = min(len(sti), cap)
+        r0 = i * cap
+        assert np.array_equal(g_sti[r0:r0 + n], sti[:n]), i
+        assert np.array_equal(g_srk[r0:r0 + n], srk[:n]), i
+        assert np.array_equal(g_sidx[r0:r0 + n], sidx[:n]), i
+        assert np.array_equal(g_sw[r0:r0 + n].view(np.uint32), sw[:n].view(np.uint32)), i
+        assert np.array_equal(g_trow[a:b], np.where(trow < cap, trow, -1)), i
+        # rows past the chunk's count are left as they were
+        assert np.all(g_sti[r0 + n:r0 + cap] == SENTINEL), i
+        assert np.all(g_sidx[r0 + n:r0 + cap] == SENTINEL), i
+
+
+@pytest.mark.parametrize("name,over,C", [
+    ("fp8_t32768", {}, 4),                       # the chunked workload (two-pass scan)
+    ("fp8_t32768", {"T": 1000}, 3),              # a ragged last chunk
+    ("skewed_t16384", {"T": 5}, 8),              # fewer tokens than chunks
+    ("skewed_t16384", {"T": 3000, "seed": 2}, 2),
+    ("uniform_t4096", {}, 16),                   # 8 destinations x 16 chunks
+    ("uniform_t4096", {"K": 2, "T": 2500}, 5),
+    ("uniform_t4096", {"K": 6, "T": 700, "seed": 3}, 7),
+    ("fp8_t32768", {"T": 65536, "seed": 1}, 4),  # 256 workgroups
+])
+def test_chunked_layout_equals_the_oracle_per_chunk(name, over, C):
+    s = spec(name, **over)
+    idx, w, cap, c, lay = _run(s, C)
+    _check(s, C, idx, w, cap, c, lay)
+
+
+def test_chunked_layout_capacity_overflow_and_bad_ids():
+    s = spec("skewed_t16384", T=4000, seed=5)
+    C = 4
+    idx, w, cap, c, lay = _run(s, C, cap=3000, bad_ids=True)
+    bad = int(((idx >= s.E) | (idx < -1)).sum())
+    _check(s, C, idx, w, cap, c, lay, bad=bad)
+
+
+def test_chunked_pipeline_uses_the_one_launch_layout():
+    """ChunkedDispatcher without exact counts takes its layouts from the one
+    launch; its chunks' layouts are the oracle's."""
+    s = spec("fp8_t32768", T=6000, H=256)
+    idx, w = make_routing(s)
+    d = ep.ChunkedDispatcher(s.T, s.K, s.H, num_local_experts=s.E_local, num_ranks=s.P,
+                             chunks=4, exact_counts=False)
+    from epgen import make_hidden
+    x = make_hidden(s)
+    d.forward(to_dev(x), to_dev(idx), to_dev(w), lambda i, rx, ri, rw: rx)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(d.bounds):
+        sti, srk, sidx, sw, trow = O.build_send_layout(idx[a:b], w[a:b], s.P, s.E_local)
+        lay = d.layouts[i]
+        assert np.array_equal(host(lay.token_row), trow)
+        assert np.array_equal(host(lay.send_token_idx)[:len(sti)], sti)
+        assert np.array_equal(host(lay.send_idx)[:len(sti)], sidx)
