@@ -165,6 +165,33 @@ int main(int argc, char** argv) {
     HIP_CHECK(hipStreamDestroy(cs));
   }
 
+  // The one-launch layout on the library's own scratch: the same outputs as
+  // the workspace call; then neither the workspace nor that scratch reports
+  // a bounded wait that gave up.
+  {
+    int32_t *d_trow2, *d_sti2, *d_sc2, *d_flags;
+    HIP_CHECK(hipMalloc(&d_trow2, TK * 4));
+    HIP_CHECK(hipMalloc(&d_sti2, cap * 4));
+    HIP_CHECK(hipMalloc(&d_sc2, size_t(P) * 4));
+    HIP_CHECK(hipMalloc(&d_flags, 8));
+    EP_CHECK(ep_dispatch_layout_noalloc(d_idx, d_w, T, K, P, El, cap, d_dest, d_iir, d_sc2,
+                                        nullptr, nullptr, d_sti2, d_srk, d_sidx, d_sw, d_trow2,
+                                        nullptr));
+    EP_CHECK(ep_workspace_status(d_ws, ws, d_flags, nullptr));
+    EP_CHECK(ep_workspace_status(nullptr, 0, d_flags + 1, nullptr));
+    HIP_CHECK(hipDeviceSynchronize());
+    std::vector<int32_t> trow3(TK), sti3(static_cast<size_t>(N)), sc3(P), flags(2);
+    HIP_CHECK(hipMemcpy(trow3.data(), d_trow2, TK * 4, hipMemcpyDeviceToHost));
+    HIP_CHECK(hipMemcpy(sti3.data(), d_sti2, size_t(N) * 4, hipMemcpyDeviceToHost));
+    HIP_CHECK(hipMemcpy(sc3.data(), d_sc2, size_t(P) * 4, hipMemcpyDeviceToHost));
+    HIP_CHECK(hipMemcpy(flags.data(), d_flags, 8, hipMemcpyDeviceToHost));
+    if (trow3 != trow || sc3 != sc || !std::equal(sti3.begin(), sti3.end(), sti.begin()))
+      return 7;
+    if (flags[0] != 0 || flags[1] != 0) return 8;
+    for (void* q : {(void*)d_trow2, (void*)d_sti2, (void*)d_sc2, (void*)d_flags})
+      HIP_CHECK(hipFree(q));
+  }
+
   std::FILE* g = std::fopen(argv[2], "wb");
   if (!g) return 1;
   const bool ok = write_all(g, &N, 1) && write_all(g, sc.data(), sc.size()) &&

@@ -108,3 +108,76 @@ def test_batched_fp8_and_regroup_graph_replays():
     for rep in _replays(step, outs):
         for got, want in zip(rep, eager):
             assert np.array_equal(got, want.view(torch.uint8).cpu().numpy())
+
+
+def test_noalloc_send_path_graph_replays():
+    """The send path on the library's own scratch (ep_dispatch_layout_noalloc),
+    the use it is for: captured with no allocation, replayed, equal to the
+    workspace call's eager result every time."""
+    s = spec("skewed_t16384", T=2500, H=512, seed=4)
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    T, K, P, El = s.T, s.K, s.P, s.E_local
+    cap = T * min(K, P)
+    d_idx, d_w, d_x = to_dev(idx), to_dev(w), to_dev(x)
+    counts, lay = ep.ep_dispatch_layout(d_idx, d_w, P, El, cap)
+    send_x = ep.ep_dispatch_permute(d_x, lay.token_row, cap)
+    out = ep.ep_combine(send_x, lay.token_row, d_w)
+    torch.cuda.synchronize()
+    N = int(counts.send_counts.sum().item())
+    eager = [lay.token_row.clone(), lay.send_token_idx[:N].clone(), counts.send_counts.clone(),
+             send_x[:N].clone(), out.clone()]
+
+    def step():
+        ep.ep_dispatch_layout_noalloc(d_idx, d_w, P, El, cap, counts=counts, out=lay)
+        ep.ep_dispatch_permute(d_x, lay.token_row, cap, out=send_x)
+        ep.ep_combine(send_x, lay.token_row, d_w, out=out)
+
+    outs = [lay.token_row, lay.send_token_idx[:N], counts.send_counts, send_x[:N], out]
+    for rep in _replays(step, outs):
+        for got, want in zip(rep, eager):
+            assert np.array_equal(got, want.view(torch.uint8).cpu().numpy())
+    assert ep.library_scratch_status() == 0
+
+
+def test_chunked_layout_graph_replays():
+    """Every chunk's counts and layout in one launch, then each chunk's fp8
+    permute and the combine of its dequantized rows, captured and replayed."""
+    s = spec("fp8_t32768", T=3000, H=512, seed=6)
+    idx, w = make_routing(s)
+    x = make_hidden(s)
+    T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, 3
+    bounds = ep.chunk_bounds(T, C)
+    cap = max((b - a) * min(K, P) for a, b in bounds)
+    d_idx, d_w, d_x = to_dev(idx), to_dev(w), to_dev(x)
+    counts, lay = ep.ep_dispatch_layout_chunked(d_idx, d_w, P, El, C, cap)
+    q = torch.empty((C * cap, H), dtype=torch.float8_e4m3fn, device="cuda")
+    sc = torch.empty((C * cap, H // 128), dtype=torch.float32, device="cuda")
+    y = torch.zeros((C * cap, H), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = ep.workspace_for(ep.ep_dispatch_layout_chunked_workspace_bytes(T, P, C), d_x.device,
+                          kind="graph_c")
+
+    def step():
+        ep.ep_dispatch_layout_chunked(d_idx, d_w, P, El, C, cap, counts=counts, out=lay,
+                                      workspace=ws)
+        for i, (a, b) in enumerate(bounds):
+            r = slice(i * cap, (i + 1) * cap)
+            ep.ep_dispatch_permute(d_x[a:b], lay.token_row[a:b], cap, fp8=True, out=q[r],
+                                   out_scale=sc[r])
+            y[r] = (q[r].float().view(cap, H // 128, 128) * sc[r][:, :, None]).view(cap, H) \
+                .to(torch.bfloat16)
+            ep.ep_combine(y[r], lay.token_row[a:b], d_w[a:b], out=out[a:b])
+
+    step()
+    torch.cuda.synchronize()
+    Ns = counts.send_counts.sum(dim=1).tolist()
+    written = [q[i * cap:i * cap + n] for i, n in enumerate(Ns)]   # rows past N untouched
+    eager = [lay.token_row.clone(), counts.send_counts.clone(), out.clone()] + \
+        [t.view(torch.uint8).clone() for t in written]
+    outs = [lay.token_row, counts.send_counts, out] + written
+    for rep in _replays(step, outs):
+        for got, want in zip(rep, eager):
+            assert np.array_equal(got, want.view(torch.uint8).cpu().numpy())
+    hdr = ws[:16].view(torch.int32).cpu().numpy()
+    assert hdr[3] == 0 and hdr[0] == hdr[2]
