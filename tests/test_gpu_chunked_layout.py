@@ -110,3 +110,26 @@ def test_chunked_pipeline_uses_the_one_launch_layout():
         assert np.array_equal(host(lay.token_row), trow)
         assert np.array_equal(host(lay.send_token_idx)[:len(sti)], sti)
         assert np.array_equal(host(lay.send_idx)[:len(sti)], sidx)
+
+
+def _random_case(seed):
+    r = np.random.default_rng(1000 + seed)
+    P = int(r.choice([1, 2, 3, 5, 8, 16, 32]))
+    C = int(r.integers(1, max(2, min(16, 512 // P)) + 1))
+    El = int(r.choice([1, 2, 3, 4, 8]))
+    K = int(r.integers(1, min(16, P * El) + 1))
+    T = int(r.choice([1, 2, 63, 64, 65, 257, 1000, 4097, 9000]))
+    routing = str(r.choice(["uniform", "zipf"]))
+    unrouted = float(r.choice([0.0, 0.05, 0.3]))
+    s = spec("skewed_t16384").replace(name=f"random{seed}", T=T, E=P * El, K=K, P=P,
+                                       routing=routing, unrouted_frac=unrouted, seed=seed)
+    worst = max((b - a) * min(K, P) for a, b in O.chunk_bounds(T, C))
+    cap = worst if r.random() < 0.7 else max(0, worst // 3)
+    return s, C, cap
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_chunked_layout_random_shapes(seed):
+    s, C, cap = _random_case(seed)
+    idx, w, cap, c, lay = _run(s, C, cap=cap)
+    _check(s, C, idx, w, cap, c, lay)
