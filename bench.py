@@ -7,8 +7,9 @@ A step is one pass of the whole hot path over one batch of seeded synthetic
 routing, with inputs already resident in HBM:
   send layouts:  counts + send layout (one launch) -> row permute -> combine
   batched:       batched prepare (zero-padded) -> combine
-  fp8 chunked:   counts (all chunks), the chunks' send layouts, then per
-                 chunk, alternating 2 streams: fp8 quantize-permute -> combine
+  fp8 chunked:   counts and every chunk's send layout (one launch), then per
+                 chunk: fp8 quantize-permute -> combine, on one stream or
+                 alternating over ``--streams`` HIP streams
 The identity expert sits between dispatch and combine: combine reads the send
 rows themselves (bf16), or the dequantized fp8 rows prepared before timing.
 
@@ -334,9 +335,9 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     """The chunked fp8 workload through the library's ChunkedDispatcher, the
     same object the parity tests run: the counts and every chunk's send
     layout in one launch with the worst-case capacities (no host sync), then
-    per chunk on alternating streams the fp8 quantize-permute and the
-    combine.  The identity expert behind fp8 returns y = bf16(decode(q) *
-    scale), built once before timing."""
+    per chunk the fp8 quantize-permute and the combine: all on the caller's
+    stream, or chunk c on stream c mod S of S streams, the caller's first.  The identity expert behind fp8 returns
+    y = bf16(decode(q) * scale), built once before timing."""
     T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, s.chunks
     disp = ep.ChunkedDispatcher(T, K, H, num_local_experts=El, num_ranks=P, chunks=C, fp8=True,
                                 streams=s.streams, exact_counts=False, device=d_x.device)
@@ -554,6 +555,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the CPU-oracle sample (default: sized for ~15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streams", type=int, default=None,
+                    help="HIP streams the chunked workload's chunks alternate over (default: "
+                         "the workload's own, 1 for fp8_t32768; 2 runs the pipelined schedule)")
     ap.add_argument("--back-to-back", action="store_true",
                     help="run the timed steps back to back under one pair of events, "
                          "without clearing the Infinity Cache between steps (by default "
@@ -590,6 +594,12 @@ def main():
         return 0
     ep.lib()                                   # fail loudly if the library is missing
     s = spec(args.workload)
+    if args.streams is not None:
+        if args.streams < 1 or s.chunks < 2:
+            print("--streams takes a count >= 1 and applies to a chunked workload",
+                  file=sys.stderr)
+            return 2
+        s = s.replace(streams=args.streams)
     log(f"[bench] workload {s.name}: T={s.T} H={s.H} E={s.E} K={s.K} P={s.P} "
         f"layout={s.layout} fp8={s.fp8} chunks={s.chunks}")
     idx, w = make_routing(s)

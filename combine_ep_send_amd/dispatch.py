@@ -139,30 +139,34 @@ class ChunkedDispatcher:
 
     Everything a forward touches is allocated once, for one shape (T, K, H,
     P, E_local, chunks): the counts, each chunk's send layout and send
-    buffer (bf16, or fp8 codes + per-128-channel scales), the workspaces and
-    the streams, so repeated forwards allocate nothing but events.
+    buffer (bf16, or fp8 codes + per-128-channel scales), the side streams
+    and (on first use) the workspaces, so repeated forwards allocate nothing
+    but events.
 
-    One forward, in enqueue order:
-      1. stream 0 waits for the caller's stream;
-      2. without ``exact_counts``: the counts of every chunk and all the
-         chunks' send layouts in ONE launch on stream 0
+    ``streams`` S counts the caller's stream: stream 0 is the stream current
+    at each forward (so the first chunk waits for nothing), and S - 1 side
+    streams are created here; chunk c runs on stream c mod S.  One forward,
+    in enqueue order:
+      1. without ``exact_counts``: the counts of every chunk and all the
+         chunks' send layouts in ONE launch on the caller's stream
          (ep_dispatch_layout_chunked), each chunk with its worst case
          T_c * min(K, P) rows, so nothing waits on the host;
-         with ``exact_counts``: one count pass over every chunk ([C, P]),
-         the counts reach the host in ONE copy and size each chunk exactly,
-         then the send layouts, chunk 0's on stream 0 and the later chunks'
-         back to back on stream 1 (latency-bound, they run while chunk 0's
-         rows stream);
-      3. chunk c on stream c mod S: the row permute, ``local_kernel(c,
-         recv_x, recv_idx, recv_w)`` (bf16 expert output [rows, H], enqueued
-         on that stream), then the weighted combine into out[start:end];
-      4. the caller's stream waits for every stream.
+         with ``exact_counts``: one count pass over every chunk ([C, P]) on
+         the caller's stream, the counts reach the host in ONE copy and size
+         each chunk exactly, then the send layouts, the first chunk's on its
+         own stream and the later chunks' back to back on the next stream
+         (latency-bound, they run while the first chunk's rows stream);
+      2. each chunk on its stream, after its layout: the row permute,
+         ``local_kernel(c, recv_x, recv_idx, recv_w)`` (bf16 expert output
+         [rows, H], enqueued on that stream), then the weighted combine into
+         out[start:end];
+      3. the caller's stream waits for the side streams.
     Chunk c+1's permute is enqueued before chunk c's combine is consumed.
     ``timer`` (start(name, stream) / stop(token)) brackets every launch with
-    events; ``serialize`` puts all of it on stream 0."""
+    events; ``serialize`` puts all of it on the caller's stream."""
 
     def __init__(self, num_tokens: int, num_topk: int, hidden: int, *, num_local_experts: int,
-                 num_ranks: int, chunks: int, fp8: bool = False, streams=2,
+                 num_ranks: int, chunks: int, fp8: bool = False, streams: int = 2,
                  exact_counts: bool = False, device=None):
         self.T, self.K, self.H = int(num_tokens), int(num_topk), int(hidden)
         self.P, self.El, self.C = int(num_ranks), int(num_local_experts), int(chunks)
@@ -172,17 +176,14 @@ class ChunkedDispatcher:
         if dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
         self.device = dev
-        if isinstance(streams, int):
-            streams = [torch.cuda.Stream(device=dev) for _ in range(streams)]
-        if not streams:
+        if int(streams) < 1:
             raise ValueError("at least one stream")
-        self.streams = list(streams)
+        self.side_streams = [torch.cuda.Stream(device=dev) for _ in range(int(streams) - 1)]
         self.bounds = chunk_bounds(self.T, self.C)
         # one row stride for every chunk: the largest chunk's worst case
         self.stride = max((e - s) * min(self.K, self.P) for s, e in self.bounds)
         self.caps = [self.stride] * self.C
         T, K, P, H = self.T, self.K, self.P, self.H
-        s0 = self.streams[0]
         self.counts = Counts(
             dest=torch.empty((T, K), dtype=torch.int32, device=dev),
             is_in_rank=torch.empty((T, P), dtype=torch.uint8, device=dev),
@@ -198,14 +199,8 @@ class ChunkedDispatcher:
             send_idx=torch.empty((rows, K), dtype=torch.int32, device=dev),
             send_w=torch.empty((rows, K), dtype=torch.float32, device=dev),
             token_row=torch.empty((T, K), dtype=torch.int32, device=dev))
-        if self.exact_counts:
-            self.ws_counts = workspace_for(ep_counts_workspace_bytes(T, P, self.El, self.C), dev,
-                                           s0, "counts")
-        else:
-            self.ws_fused = workspace_for(ep_dispatch_layout_chunked_workspace_bytes(T, P, self.C),
-                                          dev, s0, "fused")
         L = self.all_layouts
-        self.layouts, self.recv, self.ws_layout = [], [], []
+        self.layouts, self.recv = [], []
         for i, (a, b) in enumerate(self.bounds):
             r = slice(i * cap, (i + 1) * cap)
             self.layouts.append(SendLayout(L.send_token_idx[r], L.send_rank[r], L.send_idx[r],
@@ -215,15 +210,12 @@ class ChunkedDispatcher:
                                   torch.empty((cap, H // 128), dtype=torch.float32, device=dev)))
             else:
                 self.recv.append(torch.empty((cap, H), dtype=torch.bfloat16, device=dev))
-            if self.exact_counts:
-                st = self._layout_stream(i, False)
-                self.ws_layout.append(workspace_for(ep_layout_workspace_bytes(max(b - a, 1), P),
-                                                    dev, st))
+        self.layout_ws_bytes = ep_layout_workspace_bytes(max(e - s for s, e in self.bounds) or 1,
+                                                         P)
 
-    def _layout_stream(self, i: int, serialize: bool):
-        if serialize or i == 0 or len(self.streams) == 1:
-            return self.streams[0]
-        return self.streams[1]
+    def chunk_stream_index(self, i: int, nstreams: int) -> int:
+        """Index of chunk i's stream among ``nstreams`` (0 = the caller's)."""
+        return i % nstreams
 
     def forward(self, x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
                 local_kernel: Callable, *, out: Optional[torch.Tensor] = None, timer=None,
@@ -235,8 +227,9 @@ class ChunkedDispatcher:
         if out is None:
             out = torch.empty((T, H), dtype=torch.bfloat16, device=self.device)
         main = torch.cuda.current_stream(self.device)
-        streams = self.streams[:1] if serialize else self.streams
-        s0 = streams[0]
+        streams = [main] if serialize else [main] + self.side_streams
+        S = len(streams)
+        chunk_st = [streams[self.chunk_stream_index(i, S)] for i in range(self.C)]
 
         def mark(name, st):
             return timer.start(name, st) if timer is not None else None
@@ -245,39 +238,49 @@ class ChunkedDispatcher:
             if tok is not None:
                 timer.stop(tok)
 
-        start = torch.cuda.Event()
-        start.record(main)
-        s0.wait_event(start)
+        side_started = set()      # side streams that this forward has ordered after the caller
+
+        def join(st):
+            """A side stream's first work waits for what the caller enqueued."""
+            if st is not main and st not in side_started:
+                st.wait_stream(main)
+                side_started.add(st)
+
         laid = []
         if not self.exact_counts:
             # counts and every chunk's layout in one launch, no host sync
-            tk = mark("dispatch_layout", s0)
+            ws = workspace_for(ep_dispatch_layout_chunked_workspace_bytes(T, P, self.C),
+                               self.device, main, "fused")
+            tk = mark("dispatch_layout", main)
             ep_dispatch_layout_chunked(topk_idx, topk_weights, P, El, self.C, self.stride,
-                                       counts=self.counts, out=self.all_layouts,
-                                       workspace=self.ws_fused, stream=s0)
+                                       counts=self.counts, out=self.all_layouts, workspace=ws,
+                                       stream=main)
             done(tk)
-            ready = torch.cuda.Event()
-            ready.record(s0)
-            laid = [(ready, s0)] * self.C
+            ready = None
+            if any(st is not main for st in chunk_st):
+                ready = torch.cuda.Event()
+                ready.record(main)
+            laid = [(ready, main)] * self.C
         else:
-            tk = mark("counts", s0)
+            ws = workspace_for(ep_counts_workspace_bytes(T, P, El, self.C), self.device, main,
+                               "counts")
+            tk = mark("counts", main)
             ep_compute_send_counts(topk_idx, P, El, self.C, expert_counts=False,
-                                   out=self.counts, workspace=self.ws_counts, stream=s0)
+                                   out=self.counts, workspace=ws, stream=main)
             done(tk)
-            with torch.cuda.stream(s0):
-                self.caps = [int(v) for v in to_host(self.counts.send_counts).sum(dim=1)]
-            ready = torch.cuda.Event()
-            ready.record(s0)
-            for st in streams[1:]:
-                st.wait_event(ready)
+            self.caps = [int(v) for v in to_host(self.counts.send_counts).sum(dim=1)]
+            first = next((i for i, (a, b) in enumerate(self.bounds) if b > a), 0)
+            lead = chunk_st[first]
+            rest = streams[(streams.index(lead) + 1) % S]
             for i, (a, b) in enumerate(self.bounds):
-                st = self._layout_stream(i, serialize)
+                st = lead if i <= first else rest
                 if b > a:
+                    join(st)
+                    lws = workspace_for(self.layout_ws_bytes, self.device, st)
                     tk = mark("layout", st)
                     ep_build_send_layout(topk_idx[a:b], topk_weights[a:b], self.counts.dest[a:b],
                                          self.counts.send_counts[i], P, El, self.caps[i],
-                                         out=self.layouts[i], workspace=self.ws_layout[i],
-                                         stream=st)
+                                         out=self.layouts[i], workspace=lws, stream=st)
                     done(tk)
                 ev = torch.cuda.Event()
                 ev.record(st)
@@ -285,10 +288,12 @@ class ChunkedDispatcher:
         for i, (a, b) in enumerate(self.bounds):
             if b == a:
                 continue
-            st = streams[i % len(streams)]
+            st = chunk_st[i]
             ev, lst = laid[i]
-            if lst is not st:
+            if lst is not st:      # the layout ran on another stream (after the caller's work)
                 st.wait_event(ev)
+                if st is not main:
+                    side_started.add(st)
             lay = self.layouts[i]
             tk = mark("permute_fp8" if self.fp8 else "permute", st)
             if self.fp8:
@@ -305,10 +310,8 @@ class ChunkedDispatcher:
             tk = mark("combine", st)
             ep_combine(y, lay.token_row, topk_weights[a:b], out=out[a:b], stream=st)
             done(tk)
-        for st in streams:
-            fin = torch.cuda.Event()
-            fin.record(st)
-            main.wait_event(fin)
+        for st in side_started:
+            main.wait_stream(st)
         return out
 
 

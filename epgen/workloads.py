@@ -86,7 +86,7 @@ CONFIGS = {
         zipf_s=1.2, unrouted_frac=0.05, layout="expert_major", align=128),
     "fp8_t32768": WorkloadSpec(
         "fp8_t32768", T=32768, H=7168, E=256, K=8, P=32, fp8=True, chunks=4,
-        streams=2),
+        streams=1),     # the pipelined 2-stream schedule: streams=2
 }
 
 

@@ -118,3 +118,15 @@ def test_chunked_one_launch_layout_bytes_are_the_arrays():
     # send rows' metadata and token_row out
     want = _nbytes(idx, w, dest, iir, sc, *rows, np.empty((T, K), np.int32))
     assert B.bytes_dispatch_layout_chunked(T, K, P, C, N) == want
+
+
+@pytest.mark.parametrize("C,S", [(1, 1), (4, 1), (4, 2), (5, 2), (3, 3), (7, 4)])
+def test_chunk_streams_start_on_the_callers_stream(C, S):
+    """The chunked dispatcher's stream schedule: the first chunk runs on the
+    caller's stream (index 0) and neighbouring chunks alternate."""
+    from types import SimpleNamespace
+    import combine_ep_send_amd as ep
+    idx = [ep.ChunkedDispatcher.chunk_stream_index(SimpleNamespace(C=C), i, S) for i in range(C)]
+    assert idx[0] == 0
+    assert all(0 <= v < S for v in idx)
+    assert all(idx[i + 1] == (idx[i] + 1) % S for i in range(C - 1))

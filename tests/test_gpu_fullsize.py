@@ -5,9 +5,10 @@ times it, every output element compared with the oracle.
   one launch with the worst-case capacity, the (occupancy-capped) row
   permute and the combine of the send rows (identity expert);
 * batched_t8192: the expert-batched fill and the combine over it;
-* fp8_t32768: the library's ChunkedDispatcher on two HIP streams, 4 chunks,
-  worst-case capacities, the fp8 quantize-permute, an identity expert behind
-  fp8 (y = bf16(decode(q) * scale)) and the combine; run twice, as the bench
+* fp8_t32768: the library's ChunkedDispatcher, 4 chunks, worst-case
+  capacities, the fp8 quantize-permute, an identity expert behind fp8
+  (y = bf16(decode(q) * scale)) and the combine, on the caller's stream (the
+  bench's default) and alternating over 2 streams; run twice, as the bench
   does (the second forward returns the first's expert outputs), and checked
   chunk by chunk.
 The oracle's own results are computed on the host from the same seeded
@@ -100,9 +101,10 @@ def _dequantize(q, sc, H):
     return (q.float().view(n, H // 128, 128) * sc[:, :, None]).view(n, H).to(torch.bfloat16)
 
 
-@pytest.fixture(scope="module")
-def fp8_chunked():
-    s, idx, w, x = _load("fp8_t32768")
+@pytest.fixture(scope="module", params=[1, 2], ids=["1stream", "2streams"])
+def fp8_chunked(request):
+    s, idx, w, x = _load("fp8_t32768", streams=request.param)
+    print(f"  {s.streams} stream(s)", flush=True)
     T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, s.chunks
     d_idx, d_w, d_x = to_dev(idx), to_dev(w), to_dev(x)
     disp = ep.ChunkedDispatcher(T, K, H, num_local_experts=El, num_ranks=P, chunks=C,
