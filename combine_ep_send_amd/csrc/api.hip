@@ -499,7 +499,7 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   if (!sh.fits) return EP_ERR_UNSUPPORTED;
 
   // 1. one launch: counts per local expert, aligned offsets, row_map, the
-  //    source row and weight of every regrouped row
+  //    source row and weight of every regrouped row, padding rows included
   FusedArgs a{};
   a.topk_weights = recv_w;
   a.T = num_rows;
@@ -527,30 +527,17 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   a.perm_w = perm_w;
   if (launch_regroup_layout(a, unsigned(sh.groups), stream) != hipSuccess) return EP_ERR_LAUNCH;
 
-  // 2. padding rows; 3. the received rows, token-major through row_map
-  RegroupPadArgs z{};
-  z.counts = tokens_per_expert;
-  z.offsets = expert_offsets;
-  z.E_local = bins;
-  z.align = align;
-  z.capacity = capacity;
-  z.H = hidden;
-  z.perm_x = perm_x;
-  z.perm_src = perm_src;
-  z.perm_w = perm_w;
-  if (launch_regroup_pad(z, stream) != hipSuccess) return EP_ERR_LAUNCH;
-
-  RowArgs r{};
+  // 2. every regrouped row in address order: its source row, or zeros
+  GatherArgs r{};
   r.x = recv_x;
-  r.T = num_rows;
+  r.R = num_rows;
   r.H = hidden;
-  r.token_row = row_map;
-  r.K = num_topk;
+  r.perm_src = perm_src;
+  r.offsets = expert_offsets;
+  r.bins = bins;
   r.capacity = capacity;
   r.out = perm_x;
-  r.out_scale = nullptr;
-  r.sparse = false;
-  return launch_status(launch_permute_bf16(r, stream));
+  return launch_status(launch_regroup_gather(r, stream));
 }
 
 int ep_dispatch_permute(const void* x, int64_t num_tokens, int hidden, const int32_t* token_row,

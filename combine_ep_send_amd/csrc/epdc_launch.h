@@ -156,18 +156,17 @@ size_t fused_smem_bytes(int P, int E, int tiles_per_group, int waves);
 hipError_t launch_dispatch_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
 hipError_t launch_regroup_layout(const FusedArgs& a, unsigned groups, hipStream_t s);
 
-struct RegroupPadArgs {
-  const int32_t* counts;         // [E_local] rows per expert
-  const int32_t* offsets;        // [E_local+1] aligned starts
-  int E_local;
-  int align;
-  int64_t capacity;
+struct GatherArgs {
+  const void* x;                 // [R, H] bf16 received rows
+  int64_t R;
   int H;
-  void* perm_x;                  // [cap, H] bf16
-  int32_t* perm_src;             // [cap]
-  float* perm_w;                 // [cap] or null
+  const int32_t* perm_src;       // [cap] source row of each regrouped row, -1 = padding
+  const int32_t* offsets;        // [bins+1] aligned segment starts; offsets[bins] rows in use
+  int bins;
+  int64_t capacity;              // rows of out
+  void* out;                     // [cap, H] bf16
 };
-hipError_t launch_regroup_pad(const RegroupPadArgs& a, hipStream_t s);
+hipError_t launch_regroup_gather(const GatherArgs& a, hipStream_t s);
 
 // fp8 scale formats: fl32(amax/448); the smallest power of two at or above
 // it; that power as a UE8M0 byte, four packed per 32-bit word.

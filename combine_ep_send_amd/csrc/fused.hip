@@ -471,7 +471,10 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
         }
         if (b < r0 + span) {
           s_base[b] += carry + incl - v;
-          if (MODE == kFusedRegroup && g == 0) a.offsets[b] = carry + incl - v;
+          if (MODE == kFusedRegroup) {
+            s_hist[b] = carry + incl - v;     // segment start (the published row is done with)
+            if (g == 0) a.offsets[b] = carry + incl - v;
+          }
         }
         carry += __shfl(incl, kWave - 1);
       }
@@ -479,6 +482,20 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
     }
   }
   __syncthreads();
+  if (MODE == kFusedRegroup) {
+    // Padding rows [start + count, aligned end) of every segment get source
+    // -1 and weight 0, the bins dealt to the workgroups in turn.  Every index
+    // fits int32: the host bounds the rows plus their padding.
+    for (int b = g; b < P; b += G) {
+      const int64_t r0 = int64_t(s_hist[b]) + s_tot[b];
+      int64_t r1 = int64_t(s_hist[b]) + (s_tot[b] + a.align - 1) / a.align * a.align;
+      if (r1 > a.capacity) r1 = a.capacity;
+      for (int64_t r = r0 + tid; r < r1; r += BS) {
+        a.send_token_idx[r] = -1;
+        if (a.perm_w) a.perm_w[r] = 0.0f;
+      }
+    }
+  }
 
   // ---- 4. rows and scatter ------------------------------------------------------
   const uint64_t lt = lanemask_lt();
