@@ -93,10 +93,10 @@ struct FusedShape {
 // The library's own scratch on the current device (defined below).
 int library_scratch(void** out, hipStream_t stream);
 
-FusedShape fused_shape(int64_t T, int bins, int E) {
+FusedShape fused_shape(int64_t T, int bins, int E, int most) {
   FusedShape f{};
-  f.waves = fused_waves(T);
-  f.tiles = fused_tiles(T);
+  f.waves = fused_waves(T, most);
+  f.tiles = fused_tiles(T, most);
   int64_t gmax = device_cus();
   if (gmax > kMaxFusedGroups) gmax = kMaxFusedGroups;
   f.per = (f.tiles + gmax - 1) / gmax;
@@ -239,7 +239,7 @@ size_t ep_dispatch_layout_workspace_bytes(int64_t num_tokens, int num_ranks,
   if (num_tokens < 0 || num_ranks < 1 || num_local_experts < 1) return 0;
   if (num_tokens >= kMaxTokens || int64_t(num_ranks) * num_local_experts > kMaxExperts) return 0;
   const int64_t nh = int64_t(num_ranks) + int64_t(num_ranks) * num_local_experts + 1;
-  return fused_ws_bytes(num_tokens, num_ranks, nh);
+  return fused_ws_bytes(num_tokens, num_ranks, nh, kSendMaxWaves);
 }
 
 }  // extern "C"
@@ -311,7 +311,7 @@ int dispatch_layout_impl(const int64_t* topk_idx, const float* topk_weights, int
     return EP_ERR_WORKSPACE;
   }
   const int E = num_ranks * num_local_experts;
-  const FusedShape sh = fused_shape(num_tokens, num_ranks, E);
+  const FusedShape sh = fused_shape(num_tokens, num_ranks, E, kSendMaxWaves);
   if (!sh.fits) return EP_ERR_UNSUPPORTED;
   if (use_scratch) {
     st = library_scratch(&workspace, stream);
@@ -388,7 +388,7 @@ size_t ep_dispatch_layout_chunked_workspace_bytes(int64_t num_tokens, int num_ra
   if (num_tokens < 0 || num_tokens >= kMaxTokens || num_ranks < 1 || num_chunks < 1) return 0;
   const int64_t bins = int64_t(num_ranks) * num_chunks;
   if (bins > EPDC_MAX_BINS) return 0;
-  return fused_ws_bytes(num_tokens, bins, bins + 1);
+  return fused_ws_bytes(num_tokens, bins, bins + 1, kSendMaxWaves);
 }
 
 int ep_dispatch_layout_chunked(const int64_t* topk_idx, const float* topk_weights,
@@ -418,7 +418,7 @@ int ep_dispatch_layout_chunked(const int64_t* topk_idx, const float* topk_weight
           ep_dispatch_layout_chunked_workspace_bytes(num_tokens, num_ranks, num_chunks))
     return EP_ERR_WORKSPACE;
   const int bins = int(bins64);
-  const FusedShape sh = fused_shape(num_tokens, bins, 0);
+  const FusedShape sh = fused_shape(num_tokens, bins, 0, kSendMaxWaves);
   if (!sh.fits) return EP_ERR_UNSUPPORTED;
 
   FusedArgs a{};
@@ -460,7 +460,7 @@ int ep_dispatch_layout_chunked(const int64_t* topk_idx, const float* topk_weight
 
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins) {
   if (num_rows < 0 || num_rows >= kMaxTokens || num_bins < 1) return 0;
-  return fused_ws_bytes(num_rows, num_bins, int64_t(num_bins) + 1);
+  return fused_ws_bytes(num_rows, num_bins, int64_t(num_bins) + 1, kRegroupMaxWaves);
 }
 
 int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const float* recv_w,
@@ -495,7 +495,7 @@ int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx, const floa
   if (!workspace || !aligned(workspace, 256) ||
       workspace_bytes < ep_regroup_workspace_bytes(num_rows, bins))
     return EP_ERR_WORKSPACE;
-  const FusedShape sh = fused_shape(num_rows, bins, 0);
+  const FusedShape sh = fused_shape(num_rows, bins, 0, kRegroupMaxWaves);
   if (!sh.fits) return EP_ERR_UNSUPPORTED;
 
   // 1. one launch: counts per local expert, aligned offsets, row_map, the

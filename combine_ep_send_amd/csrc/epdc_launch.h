@@ -126,21 +126,30 @@ struct FusedArgs {
 constexpr int kMaxFusedGroups = 256;
 // Bins one workgroup scans in the two-pass form (at most).
 constexpr int kMaxTwoPassBins = 8;
-// Tiles of the fused launch: one token per thread of a workgroup of 1, 2 or
-// 4 waves, chosen so that about 64 tiles cover the input (small inputs then
-// spread over more compute units; large ones keep 256-token tiles).
-inline int fused_waves(int64_t T) {
+// Tiles of the fused launch: one token per thread of a workgroup of 1 to
+// `most` waves (a power of two), chosen so that about 64 tiles cover the
+// input (small inputs then spread over more compute units; large ones keep
+// big tiles).  The send layouts take at most 4 waves, the regroup (whose
+// received rows outnumber the tokens by K) up to 16: measured on the
+// expert-major regroup of 117k rows, 16-wave tiles took its launch from 690
+// to 677 us, while 8- or 16-wave tiles made the headline's send layout
+// slower (26 and 37 against 21.5 us).
+constexpr int kSendMaxWaves = 4;
+constexpr int kRegroupMaxWaves = 16;
+inline int fused_waves(int64_t T, int most) {
   const int64_t w = (T + 64 * 64 - 1) / (64 * 64);
-  return w <= 1 ? 1 : (w <= 2 ? 2 : 4);
+  int v = 1;
+  while (v < w && v < most) v <<= 1;
+  return v;
 }
-inline int64_t fused_tiles(int64_t T) {
-  const int64_t tile = int64_t(fused_waves(T)) * 64;
+inline int64_t fused_tiles(int64_t T, int most) {
+  const int64_t tile = int64_t(fused_waves(T, most)) * 64;
   const int64_t t = (T + tile - 1) / tile;
   return t > 0 ? t : 1;
 }
 // Workspace of the fused launch over T rows: header, rows, prefixes, totals.
-inline size_t fused_ws_bytes(int64_t T, int64_t bins, int64_t row_words) {
-  const int64_t tiles = fused_tiles(T);
+inline size_t fused_ws_bytes(int64_t T, int64_t bins, int64_t row_words, int most) {
+  const int64_t tiles = fused_tiles(T, most);
   const int64_t g = tiles < kMaxFusedGroups ? tiles : kMaxFusedGroups;
   return kWsHeaderBytes + size_t(g) * size_t(row_words) * 4u + size_t(g) * size_t(bins) * 4u +
          size_t(bins) * 4u;

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
     // all loads in flight together), and publishes each group's exclusive
     // prefix and the bin's total; after a second barrier every workgroup
     // reads its own prefixes and the totals (P loads each).
-    constexpr int kQ = kMaxFusedGroups / BS;       // groups per thread (at most)
+    constexpr int kQ = kMaxFusedGroups / BS > 0 ? kMaxFusedGroups / BS : 1;  // groups per thread
     const int q = (G + BS - 1) / BS;
     const int per_b = (P + G - 1) / G;
     const int b0 = g * per_b;
@@ -620,8 +620,16 @@ hipError_t launch_fused(const FusedArgs& a, unsigned groups, hipStream_t s) {
     launch_fused_nw<MODE, 1>(a, groups, smem, s);
   else if (a.waves == 2)
     launch_fused_nw<MODE, 2>(a, groups, smem, s);
-  else
+  else if (a.waves == 4)
     launch_fused_nw<MODE, 4>(a, groups, smem, s);
+  else if constexpr (MODE == kFusedRegroup) {     // the send layouts stop at 4 waves
+    if (a.waves == 8)
+      launch_fused_nw<MODE, 8>(a, groups, smem, s);
+    else
+      launch_fused_nw<MODE, 16>(a, groups, smem, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
