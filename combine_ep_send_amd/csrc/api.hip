@@ -455,6 +455,15 @@ int ep_dispatch_layout_chunked(const int64_t* topk_idx, const float* topk_weight
   a.tiles_per_group = int(sh.per);
   a.waves = sh.waves;
   set_fused_workspace(a, workspace, bins, int64_t(bins) + 1, sh.groups);
+  // Chunk-local single pass: a workgroup reads the rows of the groups one or
+  // two chunks span, for those chunks' bins, instead of the two-pass scan
+  // over every bin.  Taken while a chunk's share is within the single pass's
+  // load budget (up to 8 loads per thread).
+  const int64_t span = (sh.groups + num_chunks - 1) / num_chunks + 1;
+  if (num_chunks > 1 && span * num_ranks <= int64_t(8) * 64 * sh.waves) {
+    a.chunk_local = true;
+    a.two_pass = false;
+  }
   return launch_status(launch_dispatch_layout(a, unsigned(sh.groups), stream));
 }
 

@@ -103,6 +103,7 @@ struct FusedArgs {
   uint32_t* pref;                // [groups, P] per-group exclusive prefixes (two-pass scan)
   uint32_t* tots;                // [P] bin totals (two-pass scan)
   bool two_pass;                 // scan the rows bin by bin, with a second barrier
+  bool chunk_local;              // chunks: read only the rows of the own chunks' groups and bins
   // Chunks (send mode): the bins are (chunk, destination), chunk-major, with
   // P = C * ndest bins; chunk c = tokens [c*chunk, (c+1)*chunk), the last
   // chunk ending at T.  Rows are numbered within their chunk (capacity =

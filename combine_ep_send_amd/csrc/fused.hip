@@ -233,6 +233,20 @@ __device__ __forceinline__ void ballots(const TileSlots<KMAX>& s, int P, int wav
   }
 }
 
+// Chunks of the send mode: chunk c holds tokens [c*chunk, (c+1)*chunk), the
+// last one the rest (all of them when chunk is 0, i.e. fewer tokens than
+// chunks).  chunk_first > chunk_last marks an empty chunk.
+__device__ __forceinline__ int chunk_of(const FusedArgs& a, int64_t t) {
+  const int64_t c = a.chunk > 0 ? t / a.chunk : int64_t(a.C - 1);
+  return int(c < a.C - 1 ? c : a.C - 1);
+}
+__device__ __forceinline__ int64_t chunk_first(const FusedArgs& a, int c) {
+  return int64_t(c) * a.chunk;
+}
+__device__ __forceinline__ int64_t chunk_last(const FusedArgs& a, int c) {
+  return (c == a.C - 1 ? a.T : int64_t(c + 1) * a.chunk) - 1;
+}
+
 template <int MODE, int KMAX, int NW>
 __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a) {
   constexpr int BS = NW * kWave;        // threads per workgroup = tokens per tile
@@ -398,6 +412,44 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
       s_base[b] = int(ld_relaxed(a.pref + int64_t(g) * P + b));
       s_tot[b] = int(ld_relaxed(a.tots + b));
     }
+  } else if (a.chunk_local) {
+    // Chunks: a chunk's rows are numbered on their own, so a workgroup needs
+    // only the totals and lower-group counts of the bins of the chunks its
+    // tokens fall in, and only the groups those chunks' tokens span.
+    if (my_tiles > 0) {
+      const int64_t t_lo = tile0 * BS;
+      const int64_t t_hi = (tile1 * BS < a.T ? tile1 * BS : a.T) - 1;
+      const int c_lo = chunk_of(a, t_lo), c_hi = chunk_of(a, t_hi);
+      const int g_lo = int((chunk_first(a, c_lo) / BS) / a.tiles_per_group);
+      const int g_hi = int((chunk_last(a, c_hi) / BS) / a.tiles_per_group);
+      const int D = a.ndest;
+      const int b_lo = c_lo * D;
+      const int nb = (c_hi - c_lo + 1) * D;
+      const int n = (g_hi - g_lo + 1) * nb;
+      for (int i0 = tid; i0 < n; i0 += BS * 8) {
+        uint32_t vd[8];
+        int gd[8], bd[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * BS;
+          vd[u] = 0u;
+          gd[u] = 0;
+          bd[u] = 0;
+          if (i < n) {
+            gd[u] = g_lo + i / nb;
+            bd[u] = b_lo + i % nb;
+            vd[u] = ld_relaxed(a.rows + int64_t(gd[u]) * nh + bd[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (vd[u]) {
+            atomicAdd(&s_tot[bd[u]], int(vd[u]));
+            if (gd[u] < g) atomicAdd(&s_base[bd[u]], int(vd[u]));
+          }
+        }
+      }
+    }
   } else {
     // (group, destination) and (group, expert of the slice) pairs, all loads
     // of a batch in flight together; groups start at different rows so the
@@ -447,7 +499,18 @@ __global__ __launch_bounds__(NW * kWave) void dispatch_layout_kernel(FusedArgs a
   }
   __syncthreads();
   for (int i = tid; i < ne; i += BS) a.tokens_per_expert[e0 + i] = s_etot[i];
-  if (g == 0) {
+  if (a.chunk_local) {
+    // each chunk's counts come from the workgroup holding its first token;
+    // workgroup 0 writes the zero counts of the chunks with no token
+    for (int c = 0; c < a.C; ++c) {
+      const bool empty = chunk_first(a, c) > chunk_last(a, c);
+      const int owner = empty ? 0 : int((chunk_first(a, c) / BS) / a.tiles_per_group);
+      if (owner != g) continue;
+      for (int d = tid; d < a.ndest; d += BS)
+        a.send_counts[c * a.ndest + d] = empty ? 0 : s_tot[c * a.ndest + d];
+    }
+    if (g == 0 && tid == 0 && a.diag) a.diag[0] = s_bad;
+  } else if (g == 0) {
     for (int b = tid; b < P; b += BS) a.send_counts[b] = s_tot[b];
     if (tid == 0 && a.diag) a.diag[0] = s_bad;
   }
