@@ -191,7 +191,7 @@ struct RowArgs {
   int64_t capacity;              // rows of the destination buffer
   void* out;
   void* out_scale;               // fp8 scales (float or packed uint32) or null
-  bool sparse;                   // many tokens have no destination: look up rows first
+  bool sparse;                   // many tokens have no destination (fp8: look up rows first)
   bool capped;                   // several rows per token: cap the occupancy (dense permutes)
   int scale_fmt;                 // kScale*
   int64_t scale_block_rows;      // > 0: scales column-major per block of this many rows

@@ -67,7 +67,7 @@ __device__ __forceinline__ int token_rows(const int32_t* token_row, int64_t t, i
 // fills the data rows of the expert-batched layout (token_row then holds
 // e*max + slot).
 // ---------------------------------------------------------------------------
-template <int KMAX, int PER, bool LOAD_FIRST>
+template <int KMAX, int PER>
 __global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, int nchunks,
                                                                      int64_t item0) {
   const int lane = threadIdx.x;
@@ -75,25 +75,24 @@ __global__ __launch_bounds__(kPermuteBlock) void permute_bf16_kernel(RowArgs a, 
   const int64_t item = item0 + blockIdx.x;
   const int64_t t = udiv(item, nchunks);
   const int j0 = int(item - t * nchunks) * (kPermuteBlock * PER);
-  // LOAD_FIRST: the row is loaded before its destinations are known, so both
-  // round trips overlap; a token with no destination then wastes one load,
-  // which is why the sparse expert-batched fill looks up the rows first.
-  // The hidden row is read with plain loads and the rows are stored
-  // non-temporally: on the 16k-token scatter plain loads took the permute
-  // from 346 to 331 us (same-box A/B over two passes), while plain stores,
-  // faster still alone, left dirty lines that slowed the combine after it by
-  // as much.
+  // The row is loaded before its destinations are known, so both round
+  // trips overlap; a token with no destination then wastes one load (the
+  // sparse expert-batched fill too measured faster this way: its step 0.632
+  // against 0.637 ms when it looked the rows up first).  The hidden row is
+  // read with plain loads and the rows are stored non-temporally: on the
+  // 16k-token scatter plain loads took the permute from 346 to 331 us
+  // (same-box A/B over two passes), while plain stores, faster still alone,
+  // left dirty lines that slowed the combine after it by as much.
   const u32x4* src = static_cast<const u32x4*>(a.x) + t * H8;
   u32x4 v[PER];
   int32_t rows[KMAX];
   bool use[KMAX];
-  if (!LOAD_FIRST && token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use) == 0) return;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = j0 + i * kPermuteBlock + lane;
     if (j < H8) v[i] = src[j];
   }
-  if (LOAD_FIRST) token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
+  token_rows<KMAX>(a.token_row, t, a.K, a.capacity, rows, use);
   u32x4* dst = static_cast<u32x4*>(a.out);
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
@@ -161,7 +160,8 @@ __global__ __launch_bounds__(kWave) void permute_fp8_kernel(RowArgs a, int nchun
   const int p0 = int(item - t * nchunks) * (kWave * IT);
   // LOAD_FIRST: the row is loaded before its destinations are known (as in
   // the bf16 permute), so both round trips overlap; the sparse
-  // expert-batched fill looks the rows up first and skips tokens with none.
+  // expert-batched fill looks the rows up first and skips tokens with none
+  // (loading first made its step slower here: 0.391 against 0.385 ms).
   const u32x4* src = static_cast<const u32x4*>(a.x) + t * H8;
   int32_t rows[KMAX];
   bool use[KMAX];
@@ -543,8 +543,8 @@ constexpr int64_t max_blocks(int threads) { return int64_t(UINT32_MAX) / threads
 // chunk (caps of 7, 9 or more workgroups were slower).  Only the send
 // layout's permutes (about 7 rows per token) are capped: a copy of about one
 // row per row read measured slower capped (903 against 728 us on the
-// expert-major regroup), and the sparse expert-batched fills' workgroups
-// mostly exit at once.
+// expert-major regroup), and the sparse expert-batched fills write about
+// one row per token.
 constexpr unsigned kPermuteLdsCap = 18 * 1024;
 constexpr unsigned kFp8PermuteLdsCap = 10 * 1024;
 
@@ -579,11 +579,8 @@ void launch_permute_bf16_k(const RowArgs& a, hipStream_t s) {
   // the stores slow down.
   const int nchunks = int(((a.H >> 3) + kPermuteBlock - 1) / kPermuteBlock);
   for_each_launch(a.T * nchunks, kPermuteBlock, [&](int64_t i0, unsigned g) {
-    if (a.sparse)
-      permute_bf16_kernel<KMAX, 1, false><<<g, kPermuteBlock, 0, s>>>(a, nchunks, i0);
-    else
-      permute_bf16_kernel<KMAX, 1, true><<<g, kPermuteBlock, a.capped ? kPermuteLdsCap : 0u, s>>>(
-          a, nchunks, i0);
+    permute_bf16_kernel<KMAX, 1><<<g, kPermuteBlock, a.capped ? kPermuteLdsCap : 0u, s>>>(
+        a, nchunks, i0);
   });
 }
 
