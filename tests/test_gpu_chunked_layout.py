@@ -69,15 +69,18 @@ def _check(s, C, idx, w, cap, c, lay, bad=0):
         assert np.all(g_sidx[r0 + n:r0 + cap] == SENTINEL), i
 
 
+# The launch reads back, per workgroup, only the rows of the groups its
+# chunks span (chunk-local single pass) unless a chunk spans so many groups
+# that the two-pass scan over every bin is cheaper.
 @pytest.mark.parametrize("name,over,C", [
-    ("fp8_t32768", {}, 4),                       # the chunked workload (two-pass scan)
-    ("fp8_t32768", {"T": 1000}, 3),              # a ragged last chunk
-    ("skewed_t16384", {"T": 5}, 8),              # fewer tokens than chunks
+    ("fp8_t32768", {}, 4),                       # the chunked workload (chunk-local)
+    ("fp8_t32768", {"T": 1000}, 3),              # ragged chunks; tiles straddle chunk ends
+    ("skewed_t16384", {"T": 5}, 8),              # fewer tokens than chunks (7 empty ones)
     ("skewed_t16384", {"T": 3000, "seed": 2}, 2),
     ("uniform_t4096", {}, 16),                   # 8 destinations x 16 chunks
     ("uniform_t4096", {"K": 2, "T": 2500}, 5),
     ("uniform_t4096", {"K": 6, "T": 700, "seed": 3}, 7),
-    ("fp8_t32768", {"T": 65536, "seed": 1}, 4),  # 256 workgroups
+    ("fp8_t32768", {"T": 65536, "seed": 1}, 4),  # 256 workgroups: the two-pass scan
 ])
 def test_chunked_layout_equals_the_oracle_per_chunk(name, over, C):
     s = spec(name, **over)
