@@ -349,8 +349,9 @@ int ep_dispatch_layout_chunked(const int64_t* topk_idx, const float* topk_weight
  * Bytes of workspace ep_regroup_by_expert needs for R received rows and
  * num_bins = num_groups * E_local bins: a 256-byte header (as
  * ep_dispatch_layout's), G rows of num_bins + 1 uint32, G rows of num_bins
- * uint32 and num_bins uint32, G as for ep_dispatch_layout with T = R.  Same zero-once /
- * no-overlap rules.
+ * uint32 and num_bins uint32, G = min(256, ceil(R / tile)) with tiles of
+ * 64 * w rows, w the smallest power of two up to 16 with 64 * 64 * w >= R.
+ * Same zero-once / no-overlap rules.
  */
 size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins);
 
@@ -392,7 +393,9 @@ size_t ep_regroup_workspace_bytes(int64_t num_rows, int num_bins);
  *   row_map       [R,K] int32 out  regrouped row of each local slot, else -1
  *   workspace     ep_regroup_workspace_bytes(R, bins) bytes
  * One launch with a grid barrier (as ep_dispatch_layout: same time-out and
- * EP_ERR_UNSUPPORTED rule), then a padding kernel and the row permute.
+ * EP_ERR_UNSUPPORTED rule) for the counts, offsets, row_map, perm_src and
+ * perm_w (padding included), then one launch that writes the rows of perm_x
+ * in address order (each its source row, or zeros).
  */
 int ep_regroup_by_expert(const void* recv_x, const int32_t* recv_idx,
                          const float* recv_w, const int32_t* row_group,
