@@ -9,6 +9,7 @@ in the HIP kernels; PyTorch only supplies device memory and streams.
 from __future__ import annotations
 
 import ctypes
+import functools
 from typing import NamedTuple, Optional
 
 import torch
@@ -79,6 +80,19 @@ def _vp(t: Optional[torch.Tensor]):
 def _stream(stream) -> ctypes.c_void_p:
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on_stream(fn):
+    """An entry point given ``stream`` runs with that stream current, so the
+    outputs it allocates belong to it: the caching allocator then hands their
+    memory out again only after the work enqueued there."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return call
 
 
 def _gpu(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None) -> torch.Tensor:
@@ -198,6 +212,7 @@ def check_workspaces(*workspaces: torch.Tensor) -> None:
 # entry points
 # ---------------------------------------------------------------------------
 
+@_on_stream
 def ep_compute_send_counts(topk_idx: torch.Tensor, num_ranks: int, num_local_experts: int,
                            num_chunks: int = 1, *, expert_counts: bool = True,
                            out: Optional[Counts] = None,
@@ -233,6 +248,7 @@ def ep_compute_send_counts(topk_idx: torch.Tensor, num_ranks: int, num_local_exp
     return out
 
 
+@_on_stream
 def ep_build_send_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor,
                          dest: torch.Tensor, send_counts: torch.Tensor, num_ranks: int,
                          num_local_experts: int, num_send_capacity: int, *,
@@ -282,6 +298,7 @@ def ep_dispatch_layout_workspace_bytes(num_tokens: int, num_ranks: int,
                                                         int(num_local_experts)))
 
 
+@_on_stream
 def ep_dispatch_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor, num_ranks: int,
                        num_local_experts: int, num_send_capacity: int, *,
                        expert_counts: bool = True, counts: Optional[Counts] = None,
@@ -345,6 +362,7 @@ def ep_dispatch_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor, num_r
     return counts, out
 
 
+@_on_stream
 def ep_dispatch_layout_noalloc(topk_idx: torch.Tensor, topk_weights: torch.Tensor,
                                num_ranks: int, num_local_experts: int, num_send_capacity: int,
                                *, counts: Counts, out: SendLayout, stream=None):
@@ -403,6 +421,7 @@ def ep_dispatch_layout_chunked_workspace_bytes(num_tokens: int, num_ranks: int,
                                                                 int(num_chunks)))
 
 
+@_on_stream
 def ep_dispatch_layout_chunked(topk_idx: torch.Tensor, topk_weights: torch.Tensor,
                                num_ranks: int, num_local_experts: int, num_chunks: int,
                                chunk_capacity: int, *, counts: Optional[Counts] = None,
@@ -465,6 +484,7 @@ def ep_regroup_workspace_bytes(num_rows: int, num_bins: int) -> int:
     return int(lib().ep_regroup_workspace_bytes(int(num_rows), int(num_bins)))
 
 
+@_on_stream
 def ep_regroup_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
                          recv_w: Optional[torch.Tensor], num_local_experts: int,
                          align: int = 1, capacity: Optional[int] = None, *,
@@ -529,6 +549,7 @@ def ep_regroup_by_expert(recv_x: torch.Tensor, recv_idx: torch.Tensor,
     return out
 
 
+@_on_stream
 def ep_dispatch_permute(x: torch.Tensor, token_row: torch.Tensor, num_send_capacity: int, *,
                         fp8: bool = False, out: Optional[torch.Tensor] = None,
                         out_scale: Optional[torch.Tensor] = None, stream=None):
@@ -565,6 +586,7 @@ def ep_dispatch_permute(x: torch.Tensor, token_row: torch.Tensor, num_send_capac
     return (out, out_scale) if fp8 else out
 
 
+@_on_stream
 def ep_batched_prepare(x: torch.Tensor, topk_idx: torch.Tensor, first_expert: int,
                        num_local_experts: int, max_num_tokens: int, *,
                        out: Optional[torch.Tensor] = None,
@@ -620,6 +642,7 @@ def batched_scale_like(num_local_experts: int, max_num_tokens: int, hidden: int,
     return torch.empty((El, M, units), dtype=dt, device=device)
 
 
+@_on_stream
 def ep_batched_prepare_fp8(x: torch.Tensor, topk_idx: torch.Tensor, first_expert: int,
                            num_local_experts: int, max_num_tokens: int, *,
                            scale_fmt: str = "f32", scale_col_major: bool = False,
@@ -672,6 +695,7 @@ def ep_batched_prepare_fp8(x: torch.Tensor, topk_idx: torch.Tensor, first_expert
     return out, out_scale, tokens_per_expert, token_row
 
 
+@_on_stream
 def ep_combine(y: torch.Tensor, token_row: torch.Tensor,
                topk_weights: Optional[torch.Tensor], *, bias=None,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
