@@ -16,7 +16,8 @@
 //     starts, the rows of lower workgroups its base inside each segment.  A
 //     slice of the experts is summed by every workgroup.  With many groups
 //     and bins the rows are instead scanned bin by bin, one slice of bins
-//     per workgroup, and read back after a second barrier.
+//     per workgroup, and read back after a second barrier; with chunks, a
+//     workgroup reads only the rows of the groups its chunks span.
 //  4. It ranks its tokens again and writes token_row and the send rows
 //     token-major.
 //
