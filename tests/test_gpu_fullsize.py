@@ -209,15 +209,18 @@ def test_chunked_pipeline_fewer_tokens_than_chunks(T, fp8):
         assert np.array_equal(bits(out), ref), exact
 
 
-def test_chunked_pipeline_matches_the_oracle_per_chunk_bf16():
-    """dispatch_chunked_forward (2 streams, bf16, exact counts) equals the
-    oracle chunk by chunk."""
+@pytest.mark.parametrize("streams", [1, 2, 3])
+def test_chunked_pipeline_matches_the_oracle_per_chunk_bf16(streams):
+    """dispatch_chunked_forward (bf16, exact counts, 1 to 3 streams) equals
+    the oracle chunk by chunk."""
     s = spec("fp8_t32768", T=4096, H=1024)
     idx, w = make_routing(s)
     x = make_hidden(s)
+    print(f"case: chunked pipeline bf16 T={s.T} H={s.H} streams={streams}", flush=True)
     d_idx, d_w, d_x = to_dev(idx), to_dev(w), to_dev(x)
     out = ep.dispatch_chunked_forward(d_x, d_idx, d_w, lambda rx, ri, rw: rx,
-                                      num_local_experts=s.E_local, num_ranks=s.P, chunks=4)
+                                      num_local_experts=s.E_local, num_ranks=s.P, chunks=4,
+                                      streams=streams)
     torch.cuda.synchronize()
     ref = np.empty_like(x)
     for a, b in O.chunk_bounds(s.T, 4):
