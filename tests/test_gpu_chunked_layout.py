@@ -136,3 +136,33 @@ def test_chunked_layout_random_shapes(seed):
     s, C, cap = _random_case(seed)
     idx, w, cap, c, lay = _run(s, C, cap=cap)
     _check(s, C, idx, w, cap, c, lay)
+
+
+@pytest.mark.parametrize("streams", [1, 2])
+def test_chunked_pipeline_on_a_callers_side_stream(streams):
+    """A forward called with another stream current runs stream 0's work on
+    that stream; its result, read after that stream alone is synchronized,
+    is the oracle's, and a second forward on the default stream agrees."""
+    s = spec("fp8_t32768", T=3000, H=512, seed=4)
+    idx, w = make_routing(s)
+    from epgen import make_hidden
+    x = make_hidden(s)
+    print(f"case: chunked pipeline on a side stream T={s.T} streams={streams}", flush=True)
+    d_idx, d_w, d_x = to_dev(idx), to_dev(w), to_dev(x)
+    d = ep.ChunkedDispatcher(s.T, s.K, s.H, num_local_experts=s.E_local, num_ranks=s.P,
+                             chunks=3, streams=streams, exact_counts=False)
+    caller = torch.cuda.Stream()
+    caller.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(caller):
+        out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+        d.forward(d_x, d_idx, d_w, lambda i, rx, ri, rw: rx, out=out)
+    caller.synchronize()
+    got = host(out)
+    ref = np.empty_like(x)
+    for a, b in O.chunk_bounds(s.T, 3):
+        sti, _, _, _, trow = O.build_send_layout(idx[a:b], w[a:b], s.P, s.E_local)
+        ref[a:b] = O.combine(O.dispatch_permute(x[a:b], sti), trow, w[a:b])
+    assert np.array_equal(got, ref)
+    out2 = d.forward(d_x, d_idx, d_w, lambda i, rx, ri, rw: rx)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out2), ref)
