@@ -1,0 +1,43 @@
+"""bench.py end to end on the GPU: one short run of the tiny workload prints
+one JSON line with the fields its consumers read (metric, value, roofline,
+cpu_baseline, workspace_errors), and the figures in it are consistent."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from tests.gpu_helpers import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_prints_one_consistent_json_line():
+    print("case: bench.py --workload tiny --steps 3 --warmup 1", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                        "--steps", "3", "--warmup", "1", "--cpu-tokens", "64"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "workspace_errors"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["workspace_errors"] == 0
+    assert d["config"]["workload"] == "tiny"
+    # value is the algorithmic bytes over the step time
+    assert abs(d["value"] - d["alg_bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9) \
+        <= 0.01 * d["value"] + 0.01
+    rf = d["roofline"]
+    assert rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
