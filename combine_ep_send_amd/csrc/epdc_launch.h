@@ -225,6 +225,8 @@ hipError_t launch_scale_pad(const ScalePadArgs& a, hipStream_t s);
 constexpr int kMaxRowBlock = 1024;
 // Workgroup of the bf16 permute (one 16-byte piece per thread).
 constexpr int kPermuteBlock = 128;
+// Workgroup of the regroup's gather (one 4 KiB window of the output).
+constexpr int kGatherBlock = 256;
 // Workgroup of the combine for sparse slots (several pieces per thread).
 constexpr int kSparseBlock = 128;
 

@@ -337,27 +337,26 @@ __global__ __launch_bounds__(kBlock) void scale_pad_kernel(ScalePadArgs a) {
 // ---------------------------------------------------------------------------
 // Rows of the regrouped layout, gathered: the rows in use (expert_offsets[
 // bins] of them, at most the capacity) are written as one flat run of
-// 16-byte pieces, one workgroup of kPermuteBlock threads per 2 KiB window;
-// a piece of row n holds the same piece of received row perm_src[n], or zero
+// 16-byte pieces, one workgroup of kGatherBlock threads per 4 KiB window; a
+// piece of row n holds the same piece of received row perm_src[n], or zero
 // where the source is -1 (a padding row).  Rows past the ones in use are left
 // as they are.  The stores stream as a sequential fill would, while the
 // reads are gathered (a received row that several experts share is read
 // once per expert).  Against scattering each received row to its experts
 // (one read, scattered writes) and zeroing the padding in a kernel of its
 // own, the expert-major step measured 1.975-1.983 ms against 2.005-2.011.
-//
-// The windows start 1 KiB past a 2 KiB boundary of the address space
-// (`shift` pieces before the buffer's start): a sequential fill in 2 KiB
-// blocks so placed ran at 6.6 TB/s, against 5.5 TB/s with the blocks on
-// 2 KiB boundaries, and the regroup's gather took 664 against 676 us.
+// Windows of 4 KiB beat 2 KiB ones (a sequential fill in 2 KiB blocks runs
+// at 5.5 TB/s on 2 KiB boundaries, 6.6 TB/s 1 KiB past them, in 4 KiB blocks
+// at 6.5-6.6 TB/s wherever they start): the gather took 638-645 us against
+// 664 us for 2 KiB windows placed 1 KiB past a boundary, 676 us for a
+// workgroup per (row, 2 KiB chunk); 8 and 16 KiB windows were no faster.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kPermuteBlock) void regroup_gather_kernel(GatherArgs a, int shift,
-                                                                       int64_t item0) {
+__global__ __launch_bounds__(kGatherBlock) void regroup_gather_kernel(GatherArgs a, int64_t item0) {
   const int H8 = a.H >> 3;
-  const int64_t p = (item0 + blockIdx.x) * kPermuteBlock - shift + int(threadIdx.x);
+  const int64_t p = (item0 + blockIdx.x) * kGatherBlock + int(threadIdx.x);
   int64_t rows = a.offsets[a.bins];
   if (rows > a.capacity) rows = a.capacity;
-  if (p < 0 || p >= rows * H8) return;
+  if (p >= rows * H8) return;
   const int64_t n = udiv(p, H8);
   const int j = int(p - n * H8);
   const int32_t src = a.perm_src[n];
@@ -715,12 +714,10 @@ hipError_t launch_scale_pad(const ScalePadArgs& a, hipStream_t s) {
 
 hipError_t launch_regroup_gather(const GatherArgs& a, hipStream_t s) {
   if (a.capacity == 0) return hipSuccess;
-  // Grid over the capacity's pieces (the row count is known only on the
-  // device), in windows placed 1 KiB past a 2 KiB boundary.
-  const int shift = int(((reinterpret_cast<uintptr_t>(a.out) >> 4) - 64) & (kPermuteBlock - 1));
-  const int64_t windows = (a.capacity * (a.H >> 3) + shift + kPermuteBlock - 1) / kPermuteBlock;
-  for_each_launch(windows, kPermuteBlock, [&](int64_t i0, unsigned g) {
-    regroup_gather_kernel<<<g, kPermuteBlock, 0, s>>>(a, shift, i0);
+  // Grid over the capacity's pieces: the row count is known only on the device.
+  const int64_t windows = (a.capacity * (a.H >> 3) + kGatherBlock - 1) / kGatherBlock;
+  for_each_launch(windows, kGatherBlock, [&](int64_t i0, unsigned g) {
+    regroup_gather_kernel<<<g, kGatherBlock, 0, s>>>(a, i0);
   });
   return hipGetLastError();
 }
