@@ -227,8 +227,8 @@ constexpr int kMaxRowBlock = 1024;
 constexpr int kPermuteBlock = 128;
 // Workgroup of the regroup's gather (one 4 KiB window of the output).
 constexpr int kGatherBlock = 256;
-// Workgroup of the combine for sparse slots (several pieces per thread).
-constexpr int kSparseBlock = 128;
+// Largest workgroup of the combine for sparse slots (several pieces per thread).
+constexpr int kSparseMaxBlock = 512;
 
 struct CombineArgs {
   const void* y;

@@ -459,17 +459,19 @@ __global__ __launch_bounds__(kMaxRowBlock) void combine_kernel(CombineArgs a, in
 // ---------------------------------------------------------------------------
 // Combine for sparse slots (most tokens name one or two rows, e.g. expert
 // outputs restored onto received rows): the same sums in the same order, but
-// a thread owns PER pieces and each valid slot's row is loaded and added in
-// turn, so every wave keeps PER loads in flight instead of one.
+// a thread owns PER pieces, blockDim.x apart, and each valid slot's row is
+// loaded and added in turn, so every wave keeps PER loads in flight.
 // ---------------------------------------------------------------------------
 template <int KMAX, bool WEIGHTED, int PER>
-__global__ __launch_bounds__(kSparseBlock) void combine_sparse_kernel(CombineArgs a, int nchunks,
-                                                                      int64_t item0) {
+__global__ __launch_bounds__(kSparseMaxBlock) void combine_sparse_kernel(CombineArgs a,
+                                                                         int nchunks,
+                                                                         int64_t item0) {
 #pragma clang fp contract(off)
   const int H8 = a.H >> 3;
+  const int BS = int(blockDim.x);
   const int64_t item = item0 + blockIdx.x;
   const int64_t t = udiv(item, nchunks);
-  const int j0 = int(item - t * nchunks) * (kSparseBlock * PER) + int(threadIdx.x);
+  const int j0 = int(item - t * nchunks) * (BS * PER) + int(threadIdx.x);
   int32_t rows[KMAX];
   float wk[KMAX];
   load_slots<KMAX>(a.token_row, t, a.K, rows);
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(kSparseBlock) void combine_sparse_kernel(CombineArg
     u32x4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int j = j0 + i * kSparseBlock;
+      const int j = j0 + i * BS;
       v[i] = u32x4{0u, 0u, 0u, 0u};
       if (j < H8) v[i] = ld_stream(y + int64_t(rows[k]) * H8 + j);
     }
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(kSparseBlock) void combine_sparse_kernel(CombineArg
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int j = j0 + i * kSparseBlock;
+    const int j = j0 + i * BS;
     if (j >= H8) continue;
     if (a.bias0) add_row(acc[i], ld_stream(static_cast<const u32x4*>(a.bias0) + t * H8 + j));
     if (a.bias1) add_row(acc[i], ld_stream(static_cast<const u32x4*>(a.bias1) + t * H8 + j));
@@ -617,23 +619,28 @@ void launch_permute_fp8_k(const RowArgs& a, hipStream_t s) {
 template <int KMAX>
 void launch_combine_k(const CombineArgs& a, hipStream_t s) {
   const int64_t H8 = a.H >> 3;
-  // The sparse form, up to 7 pieces per thread (a 7168-channel row in one
-  // workgroup), keeps more bytes in flight when tokens read one or two rows:
-  // fewer than two rows per token, or more rows than the K*T slots can name
-  // (a padded buffer such as the expert-batched one, where a token reads
+  // The sparse form keeps more bytes in flight when tokens read one or two
+  // rows: fewer than two rows per token, or more rows than the K*T slots can
+  // name (a padded buffer such as the expert-batched one, where a token reads
   // only its local experts' rows: 50 against 93 us on the 8k-token batched
-  // combine).  Tokens that read many rows are faster in the dense form
-  // (312 against 360 us on the 16k-token send layout).
+  // combine).  Tokens that read many rows are faster in the dense form (312
+  // against 360 us on the 16k-token send layout).  A workgroup of up to
+  // kSparseMaxBlock threads covers the row with up to 7 pieces per thread:
+  // at 7168 channels 512 threads with 2 pieces each took the expert-major
+  // restore from 583-604 to 558-566 us and the batched combine from 50 to
+  // 45.6 us, against 128 threads with 7 pieces (256 threads: no gain; 1024
+  // threads with one piece each: 806 us).
   if (a.R < 2 * a.T || a.R > int64_t(a.K) * a.T) {
-    const int per = int((H8 + kSparseBlock - 1) / kSparseBlock) < 7
-                        ? int((H8 + kSparseBlock - 1) / kSparseBlock) : 7;
-    const int64_t nch = (H8 + int64_t(kSparseBlock) * per - 1) / (int64_t(kSparseBlock) * per);
-    for_each_launch(a.T * nch, kSparseBlock, [&](int64_t i0, unsigned g) {
-#define EPDC_SPARSE(P)                                                                    \
-  if (a.w)                                                                                \
-    combine_sparse_kernel<KMAX, true, P><<<g, kSparseBlock, 0, s>>>(a, int(nch), i0);    \
-  else                                                                                    \
-    combine_sparse_kernel<KMAX, false, P><<<g, kSparseBlock, 0, s>>>(a, int(nch), i0);
+    const int64_t w = (H8 + kWave - 1) / kWave * kWave;
+    const int threads = int(w < kSparseMaxBlock ? w : kSparseMaxBlock);
+    const int per = int((H8 + threads - 1) / threads) < 7 ? int((H8 + threads - 1) / threads) : 7;
+    const int64_t nch = (H8 + int64_t(threads) * per - 1) / (int64_t(threads) * per);
+    for_each_launch(a.T * nch, threads, [&](int64_t i0, unsigned g) {
+#define EPDC_SPARSE(P)                                                                \
+  if (a.w)                                                                            \
+    combine_sparse_kernel<KMAX, true, P><<<g, threads, 0, s>>>(a, int(nch), i0);     \
+  else                                                                                \
+    combine_sparse_kernel<KMAX, false, P><<<g, threads, 0, s>>>(a, int(nch), i0);
       switch (per) {
         case 1: EPDC_SPARSE(1) break;
         case 2: EPDC_SPARSE(2) break;

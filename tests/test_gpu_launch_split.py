@@ -2,10 +2,9 @@
 grid dimension, so a row kernel over more workgroups than that splits into
 several launches, each told its first item.  Narrow rows make such token
 counts cheap: 34 million tokens of 8 channels need 34 million 128-thread
-workgroups in the bf16 permute and the sparse combine (two launches each),
-68 million need more than one launch of the 64-thread fp8 permute and dense
-combine, and the expert-batched fills run just under and just past the
-limit.  The full outputs are checked by properties that hold at any size
+workgroups in the bf16 permute (two launches), 68 million need more than
+one launch of the 64-thread fp8 permute, dense combine and sparse combine,
+and the expert-batched fills run just under and just past the limit.  The full outputs are checked by properties that hold at any size
 (with one slot per token the permute is a scatter by a permutation and the
 unweighted combine its gather; the batched routing has closed-form counts
 and slots), and sampled tokens on both sides of each split point against
@@ -49,7 +48,7 @@ def _inputs(T, H, seed):
     return x, perm
 
 
-def test_bf16_permute_and_sparse_combine_split_launches():
+def test_bf16_permute_split_launches_and_combine():
     T, H = 34_000_000, 8
     split = LIMIT // 128                  # 128-thread workgroups, one per token
     assert T > split
@@ -70,6 +69,26 @@ def test_bf16_permute_and_sparse_combine_split_launches():
     assert np.array_equal(_bits(send_x[rows]), O.dispatch_permute(xs, np.arange(len(toks))))
     loc = np.arange(len(toks), dtype=np.int32).reshape(-1, 1)
     assert np.array_equal(_bits(out[torch.from_numpy(toks).cuda()]), O.combine_partials(xs, loc))
+
+
+def test_sparse_combine_split_launches():
+    T, H = 68_000_000, 8
+    split = LIMIT // 64                   # 8 channels: one 64-thread workgroup per token
+    assert T > split
+    print(f"case: sparse combine, T={T} H={H}", flush=True)
+    y, perm = _inputs(T, H, 14)
+    token_row = perm.view(T, 1)           # R = T rows: the sparse form
+    out = ep.ep_combine(y, token_row, None)
+    # torch's one-call gather y[perm] is not exact at this size (it differed
+    # in 2^26 rows here), so the reference is gathered 8M rows at a time
+    for a in range(0, T, 8_000_000):
+        b = min(T, a + 8_000_000)
+        assert torch.equal(out[a:b], y[perm[a:b].long()]), (a, b)
+    toks = _samples(T, split)
+    rows = host(perm)[toks]
+    ys = _bits(y[torch.from_numpy(rows.astype(np.int64)).cuda()])
+    loc = np.arange(len(toks), dtype=np.int32).reshape(-1, 1)
+    assert np.array_equal(_bits(out[torch.from_numpy(toks).cuda()]), O.combine_partials(ys, loc))
 
 
 def test_fp8_permute_split_launches():
