@@ -59,6 +59,10 @@ def _routing(T, K, R, seed, dense):
     return row
 
 
+# products and sums that overflow to infinity or meet inf - inf are the point
+# of this test: numpy's warnings about them say nothing here
+@pytest.mark.filterwarnings("ignore:overflow encountered:RuntimeWarning")
+@pytest.mark.filterwarnings("ignore:invalid value encountered:RuntimeWarning")
 @pytest.mark.parametrize("dense", [True, False])
 def test_combine_nonfinite(dense):
     T, K, H = 300, 4, 1024
