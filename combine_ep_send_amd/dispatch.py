@@ -156,12 +156,14 @@ class ChunkedDispatcher:
          each chunk exactly, then the send layouts, the first chunk's on its
          own stream and the later chunks' back to back on the next stream
          (latency-bound, they run while the first chunk's rows stream);
-      2. each chunk on its stream, after its layout: the row permute,
+      2. chunk 0's row permute; then for each chunk c, on its stream: chunk
+         c+1's row permute (on chunk c+1's stream, after its layout),
          ``local_kernel(c, recv_x, recv_idx, recv_w)`` (bf16 expert output
-         [rows, H], enqueued on that stream), then the weighted combine into
-         out[start:end];
+         [rows, H], enqueued on chunk c's stream), then chunk c's weighted
+         combine into out[start:end];
       3. the caller's stream waits for the side streams.
-    Chunk c+1's permute is enqueued before chunk c's combine is consumed.
+    So chunk c+1's dispatch is issued before chunk c's local kernel, and
+    chunk c's combine is enqueued after chunk c+1's dispatch.
     ``timer`` (start(name, stream) / stop(token)) brackets every launch with
     events; ``serialize`` puts all of it on the caller's stream."""
 
@@ -285,9 +287,10 @@ class ChunkedDispatcher:
                 ev = torch.cuda.Event()
                 ev.record(st)
                 laid.append((ev, st))
-        for i, (a, b) in enumerate(self.bounds):
-            if b == a:
-                continue
+
+        def dispatch_chunk(i):
+            """Chunk i's row permute on its stream, after its layout."""
+            a, b = self.bounds[i]
             st = chunk_st[i]
             ev, lst = laid[i]
             if lst is not st:      # the layout ran on another stream (after the caller's work)
@@ -305,8 +308,22 @@ class ChunkedDispatcher:
                 recv_x = ep_dispatch_permute(x[a:b], lay.token_row, self.caps[i],
                                              out=self.recv[i], stream=st)
             done(tk)
+            return recv_x
+
+        # Chunk i+1's dispatch is issued before chunk i's local kernel, so on
+        # separate streams the next chunk's rows stream while this chunk's
+        # expert runs; every chunk has its own send buffer, so nothing waits
+        # for the buffer to be read.  Empty chunks have no work.
+        live = [i for i, (a, b) in enumerate(self.bounds) if b > a]
+        recv = {live[0]: dispatch_chunk(live[0])} if live else {}
+        for n, i in enumerate(live):
+            if n + 1 < len(live):
+                recv[live[n + 1]] = dispatch_chunk(live[n + 1])
+            a, b = self.bounds[i]
+            st = chunk_st[i]
+            lay = self.layouts[i]
             with torch.cuda.stream(st):
-                y = local_kernel(i, recv_x, lay.send_idx, lay.send_w)
+                y = local_kernel(i, recv.pop(i), lay.send_idx, lay.send_w)
             tk = mark("combine", st)
             ep_combine(y, lay.token_row, topk_weights[a:b], out=out[a:b], stream=st)
             done(tk)

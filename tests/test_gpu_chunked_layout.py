@@ -166,3 +166,52 @@ def test_chunked_pipeline_on_a_callers_side_stream(streams):
     out2 = d.forward(d_x, d_idx, d_w, lambda i, rx, ri, rw: rx)
     torch.cuda.synchronize()
     assert np.array_equal(host(out2), ref)
+
+
+class _Recorder:
+    """A forward's timer hook that records the order in which launches are
+    issued (and records nothing on the GPU)."""
+
+    def __init__(self, log):
+        self.log = log
+
+    def start(self, name, stream):
+        self.log.append(name)
+        return None
+
+    def stop(self, token):
+        pass
+
+
+@pytest.mark.parametrize("T,C,streams", [(3000, 4, 1), (3000, 4, 2), (3, 5, 2)])
+def test_chunked_pipeline_issue_order(T, C, streams):
+    """Chunk i+1's permute is issued before chunk i's local kernel, and chunk
+    i's combine after it (axolotl dispatch_chunked_forward); chunks with no
+    token issue nothing.  The result is the oracle's."""
+    s = spec("fp8_t32768", T=T, H=512, seed=6)
+    idx, w = make_routing(s)
+    from epgen import make_hidden
+    x = make_hidden(s)
+    print(f"case: chunked pipeline issue order T={T} C={C} streams={streams}", flush=True)
+    d = ep.ChunkedDispatcher(s.T, s.K, s.H, num_local_experts=s.E_local, num_ranks=s.P,
+                             chunks=C, streams=streams, exact_counts=False)
+    log = []
+
+    def local(i, rx, ri, rw):
+        log.append(f"local{i}")
+        return rx
+
+    out = d.forward(to_dev(x), to_dev(idx), to_dev(w), local, timer=_Recorder(log))
+    torch.cuda.synchronize()
+    live = [i for i, (a, b) in enumerate(O.chunk_bounds(T, C)) if b > a]
+    want = ["dispatch_layout", "permute"]
+    for n, i in enumerate(live):
+        if n + 1 < len(live):
+            want.append("permute")
+        want += [f"local{i}", "combine"]
+    assert log == want
+    ref = np.empty_like(x)
+    for a, b in O.chunk_bounds(T, C):
+        sti, _, _, _, trow = O.build_send_layout(idx[a:b], w[a:b], s.P, s.E_local)
+        ref[a:b] = O.combine(O.dispatch_permute(x[a:b], sti), trow, w[a:b])
+    assert np.array_equal(host(out), ref)
