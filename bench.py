@@ -335,9 +335,11 @@ def build_fp8_chunked_step(torch, ep, s, d_idx, d_w, d_x):
     """The chunked fp8 workload through the library's ChunkedDispatcher, the
     same object the parity tests run: the counts and every chunk's send
     layout in one launch with the worst-case capacities (no host sync), then
-    per chunk the fp8 quantize-permute and the combine: all on the caller's
-    stream, or chunk c on stream c mod S of S streams, the caller's first.  The identity expert behind fp8 returns
-    y = bf16(decode(q) * scale), built once before timing."""
+    per chunk the fp8 quantize-permute and the combine, chunk i+1's permute
+    issued before chunk i's expert: all on the caller's stream, or chunk c on
+    stream c mod S of S streams, the caller's first.  The identity expert
+    behind fp8 returns y = bf16(decode(q) * scale), built once before
+    timing."""
     T, K, P, El, H, C = s.T, s.K, s.P, s.E_local, s.H, s.chunks
     disp = ep.ChunkedDispatcher(T, K, H, num_local_experts=El, num_ranks=P, chunks=C, fp8=True,
                                 streams=s.streams, exact_counts=False, device=d_x.device)
