@@ -1,6 +1,7 @@
 """bench.py end to end on the GPU: one short run of the tiny workload prints
 one JSON line with the fields its consumers read (metric, value, roofline,
-cpu_baseline, workspace_errors), and the figures in it are consistent."""
+cpu_baseline, workspace_errors), and the figures in it are consistent; the
+chunked fp8 workload on two streams does too."""
 
 import json
 import os
@@ -41,3 +42,24 @@ def test_bench_prints_one_consistent_json_line():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
+
+
+def test_bench_chunked_fp8_on_two_streams():
+    """The chunked fp8 workload with the configuration's two-stream schedule
+    (--streams 2): one JSON line, its config naming two streams and four
+    chunks, and no bounded wait that gave up."""
+    print("case: bench.py --workload fp8_t32768 --streams 2 --steps 2 --warmup 1", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload",
+                        "fp8_t32768", "--streams", "2", "--steps", "2", "--warmup", "1",
+                        "--no-cpu-baseline"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    assert d["config"]["workload"] == "fp8_t32768"
+    assert d["config"]["streams"] == 2 and d["config"]["chunks"] == 4
+    assert d["workspace_errors"] == 0
+    assert d["value"] > 0 and d["roofline"]["frac"] > 0
+    assert abs(d["value"] - d["alg_bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9) \
+        <= 0.01 * d["value"] + 0.01
