@@ -1,7 +1,8 @@
 """bench.py end to end on the GPU: one short run of the tiny workload prints
 one JSON line with the fields its consumers read (metric, value, roofline,
 cpu_baseline, workspace_errors), and the figures in it are consistent; the
-chunked fp8 workload on two streams does too."""
+chunked fp8 workload on two streams does too, and so do the back-to-back
+and copy-calibration modes."""
 
 import json
 import os
@@ -63,3 +64,25 @@ def test_bench_chunked_fp8_on_two_streams():
     assert d["value"] > 0 and d["roofline"]["frac"] > 0
     assert abs(d["value"] - d["alg_bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9) \
         <= 0.01 * d["value"] + 0.01
+
+
+def _one_line(args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args,
+                       cwd=ROOT, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    return json.loads(lines[0])
+
+
+def test_bench_back_to_back_and_copy_calibration():
+    """--back-to-back times uninterrupted steps with the Infinity Cache left
+    warm, and says so in its line; --copy-calibration (the reference copy the
+    rocprofv3 byte counters are scaled by) reports the bytes it moves."""
+    print("case: bench.py --workload tiny --back-to-back; --copy-calibration", flush=True)
+    d = _one_line(["--workload", "tiny", "--steps", "3", "--warmup", "1", "--back-to-back",
+                   "--no-cpu-baseline"])
+    assert d["config"]["mall_flush_between_steps"] is False
+    assert d["value"] > 0 and d["workspace_errors"] == 0
+    c = _one_line(["--copy-calibration"])
+    assert c["copy_calibration_bytes_read"] == c["copy_calibration_bytes_written"] > 0
